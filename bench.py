@@ -1,0 +1,282 @@
+"""Benchmark of the Llama-3 block library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-others]
+
+One step is one llb_block_prefill call of the Llama-3.1-8B block on B=1 x
+T=2048 tokens (RMSNorm+QKV+RoPE+cache write, causal GQA attention, O projection
++ residual, RMSNorm+gate/up+SiLU.up, down projection + residual), inputs
+resident in HBM.  Prints ONE JSON line.  Besides the headline number it
+reports:
+  * roofline: the dominant kernel (the gate/up projection), its algorithmic
+    FLOPs per launch over its average launch time, measured with HIP events on
+    the launch stream over the timed region, against the bf16 MFMA peak;
+  * cpu_baseline: the fp64 CPU oracle timed on the host on the same workload;
+  * other_workloads: 8B decode (B=32, P=1000), 70B decode (B=64, P=4096) and 70B
+    prefill (B=1, T=16384), each timed the same way (decode with two weight and
+    cache sets used alternately so that the 256 MB last-level cache cannot hold
+    the working set between steps), with per-stage times.
+Inputs are seeded synthetic tensors with the workload's shapes and
+distributions; nothing is read from disk.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Llama-3 block tok/s; decode HBM GB/s and prefill MFMA TFLOP/s vs peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+HEADLINE = "8b_bf16_prefill"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------- algorithmic work
+def stage_flops(wl):
+    """Algorithmic FLOPs per stage: 2 per multiply-add of each projection; attention
+    4*hd*n_heads per visible (query, key) pair (Q.K and P.V), causal pairs only."""
+    s = wl.shape
+    M = wl.B * wl.T
+    d, hd, f = s.d_model, s.head_dim, s.d_ff
+    if wl.mode == "prefill":
+        pairs = wl.B * wl.T * (wl.T + 1) // 2
+    else:
+        pairs = wl.B * (wl.P + 1)
+    return {
+        "qkv": 2 * M * d * (s.n_heads + 2 * s.n_kv_heads) * hd,
+        "attention": 4 * hd * s.n_heads * pairs,
+        "o_proj": 2 * M * s.n_heads * hd * d,
+        "gate_up": 2 * M * d * 2 * f,
+        "down": 2 * M * f * d,
+    }
+
+
+def stage_bytes(wl):
+    """Algorithmic HBM bytes per stage: each weight once, norm gains, KV rows read
+    (P cached rows) and written (new rows), x read and y written."""
+    s = wl.shape
+    es = 2 if s.dtype == "bf16" else 4
+    M = wl.B * wl.T
+    d, hd, f = s.d_model, s.head_dim, s.d_ff
+    kv_row = s.n_kv_heads * hd * es
+    return {
+        "qkv": (s.n_heads + 2 * s.n_kv_heads) * hd * d * es + d * es + M * d * 4 + 2 * M * kv_row,
+        "attention": 2 * wl.B * wl.P * kv_row,
+        "o_proj": d * s.n_heads * hd * es,
+        "gate_up": 2 * f * d * es + d * es,
+        "down": d * f * es + M * d * 4,
+    }
+
+
+# ------------------------------------------------------------- GPU timing
+def time_workload(name, steps, warmup, sets=1):
+    import torch
+    import workloads
+    from dense_decoder_only_amd import llb
+
+    wl = workloads.get(name)
+    shp = wl.shape
+    dev = "cuda"
+    cap = workloads.cache_capacity(wl.P + wl.T)
+    log(f"{name}: building {sets} weight/cache set(s) on the GPU")
+    blocks, caches = [], []
+    w, gen = workloads.make_weights(shp, wl.seed, device=dev)
+    x = workloads.make_x(wl.B, wl.T, shp.d_model, gen, device=dev)
+    for i in range(sets):
+        blocks.append(llb.llb_block_create(llb.make_config(shp, cap), w))
+        kc, vc = workloads.make_cache(shp, wl.B, wl.P, cap, gen, device=dev)
+        caches.append((kc, vc))
+    del w
+    y = torch.empty_like(x)
+    ws = llb.workspace(blocks[0], wl.B, wl.T)
+    torch.cuda.synchronize()
+
+    def step(i):
+        blk = blocks[i % sets]
+        kc, vc = caches[i % sets]
+        if wl.mode == "prefill":
+            llb.llb_block_prefill(blk, x, y, wl.B, wl.T, kc, vc, cap, ws)
+        else:
+            llb.llb_block_decode(blk, x, y, wl.B, wl.P, kc, vc, cap, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for b in blocks:
+        llb.llb_block_set_stage_timing(b, True)
+        llb.llb_block_stage_times(b)           # clear
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    stage_ms = {k: 0.0 for k in llb.STAGES}
+    calls = 0
+    for b in blocks:
+        ms, n = llb.llb_block_stage_times(b)
+        llb.llb_block_set_stage_timing(b, False)
+        for k in stage_ms:
+            stage_ms[k] += ms[k]
+        calls += n
+    for b in blocks:
+        llb.llb_block_destroy(b)
+    del caches, x, y, ws
+    torch.cuda.empty_cache()
+    per_call = {k: v / calls for k, v in stage_ms.items()}
+    return wl, total_ms / steps, per_call
+
+
+def summarize(wl, ms, stage_ms):
+    fl = stage_flops(wl)
+    by = stage_bytes(wl)
+    tok = wl.B * wl.T
+    out = {
+        "tokens_per_s": tok / (ms * 1e-3),
+        "ms_per_step": ms,
+        "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+    }
+    if wl.mode == "prefill":
+        total = sum(fl.values())
+        out["tflops"] = total / (ms * 1e-3) / 1e12
+        out["frac_bf16_peak"] = out["tflops"] / PEAK_BF16_TFLOPS
+        out["stage_tflops"] = {k: round(fl[k] / (stage_ms[k] * 1e-3) / 1e12, 2) for k in fl}
+    else:
+        total = sum(by.values())
+        out["hbm_gbs"] = total / (ms * 1e-3) / 1e9
+        out["frac_hbm_peak"] = out["hbm_gbs"] / PEAK_HBM_GBS
+        out["algorithmic_bytes"] = total
+        out["stage_gbs"] = {k: round(by[k] / (stage_ms[k] * 1e-3) / 1e9, 1) for k in by}
+    return out
+
+
+# ------------------------------------------------------------- CPU oracle baseline
+def cpu_baseline(name):
+    import numpy as np  # noqa: F401
+    import threadpoolctl
+    import oracle
+    import workloads
+
+    wl = workloads.get(name)
+    log(f"cpu baseline: generating {name} inputs on the host")
+    inp = workloads.make_inputs(wl)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    log(f"cpu baseline: oracle on {threads} BLAS threads")
+    t0 = time.perf_counter()
+    oracle.block_forward(wl.shape, inp["weights"], inp["x"], inp["k_cache"], inp["v_cache"], wl.P)
+    dt = time.perf_counter() - t0
+    return {"value": wl.B * wl.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full {name} block forward (B={wl.B}, T={wl.T}) in float64 numpy, "
+                      f"{dt:.1f} s wall"}
+
+
+def traffic_from_profile(kernel_key):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE for the
+    current kernel source, if such a record exists (profiles/traffic.json)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec:
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "dense_decoder_only_amd", "csrc", rec["source"])
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return rec["bytes_per_launch"] if h == rec.get("source_sha") else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--only", default=None, help="time only this workload (diagnostics)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the block runs on one "
+              "device and no multi-GPU path exists", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "no GPU"
+    torch.cuda.set_device(0)
+
+    name = args.only or HEADLINE
+    wl, ms, st = time_workload(name, args.steps, args.warmup)
+    head = summarize(wl, ms, st)
+    log(f"{name}: {ms:.3f} ms/step, {head['tokens_per_s']:.0f} tok/s")
+
+    fl = stage_flops(wl)
+    dom = "gate_up"
+    if wl.mode == "prefill":
+        achieved = fl[dom] / (st[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "gemm_bf16_kernel (gate/up projection, RMSNorm + SiLU.up fused)",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "flops_per_launch": fl[dom], "avg_launch_ms": round(st[dom], 5),
+                "traffic": traffic_from_profile("gate_up_8b_prefill")}
+    else:
+        by = stage_bytes(wl)
+        achieved = by[dom] / (st[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "gemv_bf16_kernel (gate/up projection)",
+                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "bytes_per_launch": by[dom],
+                "avg_launch_ms": round(st[dom], 5), "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": wl.B, "T": wl.T, "P": wl.P, "d_model": wl.shape.d_model,
+                   "n_heads": wl.shape.n_heads, "n_kv_heads": wl.shape.n_kv_heads,
+                   "head_dim": wl.shape.head_dim, "d_ff": wl.shape.d_ff, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "headline_detail": head,
+    }
+
+    if not args.no_others and args.only is None:
+        others = {}
+        for other, sets in (("8b_bf16_decode", 2), ("70b_bf16_decode", 2), ("70b_bf16_prefill", 1)):
+            steps = args.steps if "decode" in other else max(3, args.steps // 4)
+            owl, oms, ost = time_workload(other, steps, max(2, args.warmup // 2), sets=sets)
+            others[other] = summarize(owl, oms, ost)
+            log(f"{other}: {oms:.3f} ms/step")
+        result["other_workloads"] = others
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(name)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

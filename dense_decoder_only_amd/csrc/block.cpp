@@ -1,0 +1,561 @@
+// Host side of the block library: argument validation, weight repacking, the
+// RoPE table, workspace planning and the kernel sequence of one block call.
+// Public interface: include/llb.h.
+#include "llb.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr uint64_t kMagic = 0x4b434f4c42424c4cull;  // "LLBBLOCK"
+constexpr uint64_t kDead = 0xdeadbeefdeadbeefull;
+
+llb_status fail(llb_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+llb_status fail(llb_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+llb_status hip_fail(hipError_t e, const char* what) {
+    return fail(LLB_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+constexpr double kPi = 3.14159265358979323846;
+
+}  // namespace
+
+struct llb_block {
+    uint64_t magic;
+    llb_config cfg;
+    int es;          // bytes per weight / cache element
+    int device;
+    void* wqkv;      // [(n_heads + 2 n_kv) hd, d]: Q rows, then K, then V
+    void* wo;        // [d, n_heads hd]
+    void* wgu;       // [2 d_ff, d]: 64-row groups [gate 32 rows | up 32 rows]
+    void* wdown;     // [d, d_ff]
+    float* g1;       // attention RMSNorm gain, fp32 [d]
+    float* g2;       // FFN RMSNorm gain, fp32 [d]
+    float2* rope;    // [max_positions][hd/2] (cos, sin)
+    int tile_qkv, tile_o, tile_gu, tile_down;  // bf16 prefill tile choice per projection (-1 = pick by M)
+    int timing;                      // record stage events on every call
+    std::vector<hipEvent_t> events;  // 6 per recorded call
+    size_t events_used;
+};
+
+namespace {
+
+bool handle_ok(const llb_block* b) { return b != nullptr && b->magic == kMagic; }
+
+llb_status check_config(const llb_config* c) {
+    if (!c) return fail(LLB_E_INVALID, "config is NULL");
+    if (c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->d_ff <= 0)
+        return fail(LLB_E_INVALID, "dimensions must be positive");
+    if (c->n_heads % c->n_kv_heads != 0)
+        return fail(LLB_E_INVALID, "n_heads (%d) is not a multiple of n_kv_heads (%d)", c->n_heads,
+                    c->n_kv_heads);
+    if (!(c->eps >= 0.0f) || !std::isfinite(c->eps)) return fail(LLB_E_INVALID, "eps must be >= 0");
+    if (!(c->rope_theta > 1.0f) || !std::isfinite(c->rope_theta))
+        return fail(LLB_E_INVALID, "rope_theta must be > 1");
+    if (c->max_positions <= 0) return fail(LLB_E_INVALID, "max_positions must be positive");
+    if (c->wdtype != LLB_F32 && c->wdtype != LLB_BF16) return fail(LLB_E_INVALID, "unknown wdtype");
+    if (c->rope_scaling != 0 && c->rope_scaling != 1) return fail(LLB_E_INVALID, "rope_scaling must be 0 or 1");
+    if (c->rope_scaling == 1) {
+        if (!(c->rs_factor > 0.0f) || !(c->rs_low_freq_factor > 0.0f) ||
+            !(c->rs_high_freq_factor > c->rs_low_freq_factor) || c->rs_orig_max_pos <= 0)
+            return fail(LLB_E_INVALID, "llama3 scaling needs factor > 0, 0 < low < high, orig > 0");
+    }
+    const int G = c->n_heads / c->n_kv_heads;
+    if (G > 16) return fail(LLB_E_UNSUPPORTED, "n_heads / n_kv_heads = %d > 16", G);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(LLB_E_UNSUPPORTED, "head_dim %d not in {64, 128}", c->head_dim);
+    if (c->d_model % 64 != 0 || c->d_ff % 64 != 0)
+        return fail(LLB_E_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
+    if (c->wdtype == LLB_BF16) {
+        if (c->head_dim != 128) return fail(LLB_E_UNSUPPORTED, "bf16 blocks need head_dim 128");
+        if (G > 8) return fail(LLB_E_UNSUPPORTED, "bf16 blocks need n_heads / n_kv_heads <= 8");
+        if (c->d_model % 256 != 0 || c->d_ff % 256 != 0 || c->n_heads % 2 != 0)
+            return fail(LLB_E_UNSUPPORTED,
+                        "bf16 blocks need d_model, d_ff multiples of 256 and even n_heads");
+    }
+    return LLB_OK;
+}
+
+// RoPE table: omega_i = 1/theta^(2i/hd) as float32 (power in double rounded to
+// float, then a float reciprocal), optional llama3 band scaling in double
+// rounded to float, angle = float(pos) * omega_i in float, cos/sin of that
+// angle in double rounded to float.
+std::vector<float2> build_rope_table(const llb_config& c) {
+    const int half = c.head_dim / 2;
+    std::vector<float> inv(half);
+    for (int i = 0; i < half; ++i) {
+        const float p = (float)std::pow((double)c.rope_theta, 2.0 * i / c.head_dim);
+        inv[i] = 1.0f / p;
+    }
+    if (c.rope_scaling == 1) {
+        const double factor = c.rs_factor, lo = c.rs_low_freq_factor, hi = c.rs_high_freq_factor;
+        const double orig = c.rs_orig_max_pos;
+        const double low_wavelen = orig / lo, high_wavelen = orig / hi;
+        for (int i = 0; i < half; ++i) {
+            const double w = inv[i];
+            const double wavelen = 2.0 * kPi / w;
+            double nw;
+            if (wavelen < high_wavelen) {
+                nw = w;
+            } else if (wavelen > low_wavelen) {
+                nw = w / factor;
+            } else {
+                const double s = (orig / wavelen - lo) / (hi - lo);
+                nw = (1.0 - s) * w / factor + s * w;
+            }
+            inv[i] = (float)nw;
+        }
+    }
+    std::vector<float2> t((size_t)c.max_positions * half);
+    for (int p = 0; p < c.max_positions; ++p) {
+        const float fp = (float)p;
+        for (int i = 0; i < half; ++i) {
+            volatile float ang = fp * inv[i];  // one float multiply, no contraction
+            const double a = (double)ang;
+            t[(size_t)p * half + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+        }
+    }
+    return t;
+}
+
+void free_block(llb_block* b) {
+    if (!b) return;
+    void* ptrs[] = {b->wqkv, b->wo, b->wgu, b->wdown, b->g1, b->g2, b->rope};
+    for (void* p : ptrs)
+        if (p) (void)hipFree(p);
+    for (hipEvent_t ev : b->events) (void)hipEventDestroy(ev);
+    b->events.clear();
+}
+
+// Next stage-boundary event of a recorded call (the pool grows on demand).
+hipError_t stage_event(llb_block* b, hipStream_t s) {
+    if (!b->timing) return hipSuccess;
+    if (b->events_used == b->events.size()) {
+        hipEvent_t ev;
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) return e;
+        b->events.push_back(ev);
+    }
+    return hipEventRecord(b->events[b->events_used++], s);
+}
+
+struct WsPlan {
+    size_t q = 0, o = 0, h = 0, u = 0, scratch = 0, total = 0;
+    size_t scratch_bytes = 0;
+};
+
+// Workspace layout for one call: Q_r, O, h, u, then a scratch area (split-K
+// partials of the decode projections, decode-attention partials).
+WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
+    const llb_config& c = b->cfg;
+    const size_t es = b->es;
+    const size_t M = (size_t)B * T;
+    WsPlan p;
+    size_t off = 0;
+    p.q = off; off += align_up((size_t)B * c.n_heads * T * c.head_dim * es);
+    p.o = off; off += align_up(M * c.n_heads * c.head_dim * es);
+    p.h = off; off += align_up(M * c.d_model * sizeof(float));
+    p.u = off; off += align_up(M * c.d_ff * es);
+    p.scratch = off;
+    size_t scratch = 0;
+    if (decode && c.wdtype == LLB_BF16) {
+        const int d = c.d_model, hq = c.n_heads * c.head_dim;
+        const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+        if (B <= 64) {
+            const int shapes[4][2] = {{nqkv, d}, {d, hq}, {2 * c.d_ff, d}, {d, c.d_ff}};
+            for (auto& s : shapes) {
+                const int sp = llb::gemv_bf16_splits(B, s[0], s[1]);
+                const size_t need = llb::gemv_bf16_ws_bytes(B, s[0], sp);
+                if (need > scratch) scratch = need;
+            }
+        }
+        const size_t att = llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys);
+        if (att > scratch) scratch = att;
+    }
+    p.scratch_bytes = scratch;
+    off += align_up(scratch);
+    p.total = off;
+    return p;
+}
+
+// Picks the prefill tile configuration with the best last-wave utilisation of
+// the 256 compute units; ties go to the larger tile.
+int pick_tile(int M, int N) {
+    int best = -1;
+    double best_eff = -1.0;
+    long best_area = 0;
+    for (int cfg = 0; cfg < llb::gemm_bf16_num_tile_cfgs(); ++cfg) {
+        int bm, bn, nt;
+        llb::gemm_bf16_tile(cfg, &bm, &bn, &nt);
+        if (N % bn != 0) continue;
+        const long tiles = (long)((M + bm - 1) / bm) * (N / bn);
+        const int per_cu = (bm * bn >= 256 * 128) ? 1 : 2;
+        const long slots = 256L * per_cu;
+        const long waves = (tiles + slots - 1) / slots;
+        const double eff = (double)tiles / (double)(waves * slots) *
+                           ((double)M / (double)(((M + bm - 1) / bm) * bm));
+        const long area = (long)bm * bn;
+        if (eff > best_eff + 0.02 || (eff > best_eff - 0.02 && area > best_area)) {
+            if (eff > best_eff) best_eff = eff;
+            best = cfg;
+            best_area = area;
+        }
+    }
+    return best;
+}
+
+llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, float* scratch,
+                    int tile_override, hipStream_t s, const char* what) {
+    hipError_t e;
+    if (b->cfg.wdtype == LLB_F32) {
+        e = llb::gemm_f32_launch(a, s);
+    } else if (small_m) {
+        const int sp = llb::gemv_bf16_splits(a.M, a.N, a.K);
+        e = llb::gemv_bf16_launch(a, sp, scratch, s);
+    } else {
+        const int t = tile_override >= 0 ? tile_override : pick_tile(a.M, a.N);
+        if (t < 0) return fail(LLB_E_UNSUPPORTED, "%s: no tile fits N=%d", what, a.N);
+        e = llb::gemm_bf16_launch(a, t, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, what);
+    return LLB_OK;
+}
+
+// The kernel sequence of one block call over M = B*T tokens at positions
+// pos0..pos0+T-1 ("Llama 3.1 70B", section "Transformer layer").
+llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int pos0, void* kc,
+                     void* vc, int cap, void* ws, size_t ws_bytes, hipStream_t s, bool decode) {
+    const llb_config& c = b->cfg;
+    const int L = pos0 + T;
+    const WsPlan p = plan_ws(b, B, T, decode, L);
+    if (ws_bytes < p.total)
+        return fail(LLB_E_INVALID, "workspace too small: %zu < %zu bytes", ws_bytes, p.total);
+    char* w = (char*)ws;
+    void* q = w + p.q;
+    void* o = w + p.o;
+    float* h = (float*)(w + p.h);
+    void* u = w + p.u;
+    float* scratch = (float*)(w + p.scratch);
+    const int M = B * T;
+    const int d = c.d_model, hd = c.head_dim;
+    const bool small_m = decode && M <= 64;
+
+    llb::Epilogue e{};
+    e.rope = b->rope;
+    e.T = T; e.pos0 = pos0; e.cap = cap; e.n_heads = c.n_heads; e.n_kv = c.n_kv_heads; e.hd = hd;
+
+    hipError_t te = stage_event(b, s);
+    if (te != hipSuccess) return hip_fail(te, "stage timing");
+
+    // 1. RMSNorm(x) . Wqkv^T, RoPE, Q -> workspace, K/V -> cache rows pos0..pos0+T-1
+    llb::GemmArgs a{};
+    a.A = x; a.gain = b->g1; a.W = b->wqkv; a.M = M; a.N = (c.n_heads + 2 * c.n_kv_heads) * hd;
+    a.K = d; a.norm = 1; a.eps = c.eps;
+    a.epi = e; a.epi.kind = llb::EPI_QKV; a.epi.q_out = q; a.epi.k_cache = kc; a.epi.v_cache = vc;
+    llb_status st = run_proj(b, a, small_m, scratch, b->tile_qkv, s, "qkv projection");
+    if (st != LLB_OK) return st;
+    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+
+    // 2. attention over cache rows 0..pos0+t
+    llb::AttnArgs at{};
+    at.q = q; at.k_cache = kc; at.v_cache = vc; at.o = o; at.B = B; at.T = T; at.pos0 = pos0;
+    at.cap = cap; at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads; at.hd = hd;
+    hipError_t he;
+    if (c.wdtype == LLB_F32) he = llb::attn_f32_launch(at, s);
+    else if (decode) he = llb::attn_decode_bf16_launch(at, scratch, s);
+    else he = llb::attn_prefill_bf16_launch(at, s);
+    if (he != hipSuccess) return hip_fail(he, "attention");
+    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+
+    // 3. h = x + O . Wo^T
+    a = llb::GemmArgs{};
+    a.A = o; a.W = b->wo; a.M = M; a.N = d; a.K = c.n_heads * hd; a.norm = 0; a.eps = c.eps;
+    a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = x; a.epi.out = h;
+    st = run_proj(b, a, small_m, scratch, b->tile_o, s, "output projection");
+    if (st != LLB_OK) return st;
+    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+
+    // 4. u = SiLU(RMSNorm(h) . Wgate^T) * (RMSNorm(h) . Wup^T)
+    a = llb::GemmArgs{};
+    a.A = h; a.gain = b->g2; a.W = b->wgu; a.M = M; a.N = 2 * c.d_ff; a.K = d; a.norm = 1;
+    a.eps = c.eps; a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
+    st = run_proj(b, a, small_m, scratch, b->tile_gu, s, "gate/up projection");
+    if (st != LLB_OK) return st;
+    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+
+    // 5. y = h + u . Wdown^T
+    a = llb::GemmArgs{};
+    a.A = u; a.W = b->wdown; a.M = M; a.N = d; a.K = c.d_ff; a.norm = 0; a.eps = c.eps;
+    a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = h; a.epi.out = y;
+    st = run_proj(b, a, small_m, scratch, b->tile_down, s, "down projection");
+    if (st != LLB_OK) return st;
+    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+    return LLB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* llb_last_error(void) { return g_err.c_str(); }
+
+llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* stream,
+                            llb_block** out) {
+    if (!out) return fail(LLB_E_INVALID, "out is NULL");
+    *out = nullptr;
+    llb_status st = check_config(cfg);
+    if (st != LLB_OK) return st;
+    if (!w || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->ffn_norm || !w->w_gate ||
+        !w->w_up || !w->w_down)
+        return fail(LLB_E_INVALID, "a weight pointer is NULL");
+    const llb_config& c = *cfg;
+    hipStream_t s = (hipStream_t)stream;
+
+    llb_block* b = new (std::nothrow) llb_block();
+    if (!b) return fail(LLB_E_NOMEM, "host allocation failed");
+    b->cfg = c;
+    b->es = c.wdtype == LLB_BF16 ? 2 : 4;
+    b->tile_qkv = b->tile_o = b->tile_gu = b->tile_down = -1;
+    b->timing = 0;
+    b->events_used = 0;
+    hipError_t e = hipGetDevice(&b->device);
+    if (e != hipSuccess) { delete b; return hip_fail(e, "hipGetDevice"); }
+
+    const size_t es = b->es, d = c.d_model, hd = c.head_dim, dff = c.d_ff;
+    const size_t nq = (size_t)c.n_heads * hd, nkv = (size_t)c.n_kv_heads * hd;
+    struct { void** p; size_t n; } allocs[] = {
+        {&b->wqkv, (nq + 2 * nkv) * d * es}, {&b->wo, d * nq * es}, {&b->wgu, 2 * dff * d * es},
+        {&b->wdown, d * dff * es},          {(void**)&b->g1, d * 4}, {(void**)&b->g2, d * 4},
+        {(void**)&b->rope, (size_t)c.max_positions * (hd / 2) * sizeof(float2)}};
+    for (auto& a : allocs) {
+        e = hipMalloc(a.p, a.n);
+        if (e != hipSuccess) {
+            free_block(b);
+            delete b;
+            return fail(LLB_E_NOMEM, "hipMalloc(%zu) failed: %s", a.n, hipGetErrorString(e));
+        }
+    }
+
+    auto cpy = [&](void* dst, const void* src, size_t n) {
+        if (e == hipSuccess) e = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s);
+    };
+    cpy(b->wqkv, w->wq, nq * d * es);
+    cpy((char*)b->wqkv + nq * d * es, w->wk, nkv * d * es);
+    cpy((char*)b->wqkv + (nq + nkv) * d * es, w->wv, nkv * d * es);
+    cpy(b->wo, w->wo, d * nq * es);
+    cpy(b->wdown, w->w_down, d * dff * es);
+    // gate/up interleave: 32-row groups of gate and up alternate
+    if (e == hipSuccess)
+        e = hipMemcpy2DAsync(b->wgu, 64 * d * es, w->w_gate, 32 * d * es, 32 * d * es, dff / 32,
+                             hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpy2DAsync((char*)b->wgu + 32 * d * es, 64 * d * es, w->w_up, 32 * d * es,
+                             32 * d * es, dff / 32, hipMemcpyDeviceToDevice, s);
+    // gains: widen to fp32 on the host (bf16 -> fp32 is exact)
+    std::vector<unsigned char> graw(d * es);
+    std::vector<float> gf(d);
+    const void* gsrc[2] = {w->attn_norm, w->ffn_norm};
+    float* gdst[2] = {b->g1, b->g2};
+    for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+        e = hipMemcpyAsync(graw.data(), gsrc[k], d * es, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) break;
+        for (size_t i = 0; i < d; ++i) {
+            if (es == 4) {
+                std::memcpy(&gf[i], &graw[4 * i], 4);
+            } else {
+                uint16_t hbits;
+                std::memcpy(&hbits, &graw[2 * i], 2);
+                uint32_t u = (uint32_t)hbits << 16;
+                std::memcpy(&gf[i], &u, 4);
+            }
+        }
+        e = hipMemcpyAsync(gdst[k], gf.data(), d * 4, hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+    }
+    if (e == hipSuccess) {
+        std::vector<float2> rope = build_rope_table(c);
+        e = hipMemcpyAsync(b->rope, rope.data(), rope.size() * sizeof(float2),
+                           hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+    }
+    if (e != hipSuccess) {
+        free_block(b);
+        delete b;
+        return hip_fail(e, "weight upload");
+    }
+    b->magic = kMagic;
+    *out = b;
+    return LLB_OK;
+}
+
+llb_status llb_block_destroy(llb_block* b) {
+    if (!b) return LLB_OK;
+    if (b->magic != kMagic) return fail(LLB_E_INVALID, "not a live block handle");
+    (void)hipDeviceSynchronize();
+    free_block(b);
+    b->magic = kDead;
+    delete b;
+    return LLB_OK;
+}
+
+size_t llb_block_workspace_bytes(const llb_block* b, int32_t B, int32_t T) {
+    if (!handle_ok(b) || B <= 0 || T <= 0) return 0;
+    size_t n = plan_ws(b, B, T, false, T).total;
+    if (T == 1) {
+        const size_t dn = plan_ws(b, B, 1, true, b->cfg.max_positions).total;
+        if (dn > n) n = dn;
+    }
+    return n;
+}
+
+static llb_status check_call(const llb_block* b, const void* x, const void* y, int B, int T,
+                             const void* kc, const void* vc, int cap, const void* ws) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!x || !y || !kc || !vc || !ws) return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (B <= 0 || T <= 0) return fail(LLB_E_INVALID, "B and T must be positive");
+    if (cap <= 0) return fail(LLB_E_INVALID, "cache_cap must be positive");
+    return LLB_OK;
+}
+
+llb_status llb_block_prefill(llb_block* b, const float* x, float* y, int32_t B, int32_t T,
+                             void* k_cache, void* v_cache, int32_t cache_cap, void* ws,
+                             size_t ws_bytes, void* stream) {
+    llb_status st = check_call(b, x, y, B, T, k_cache, v_cache, cache_cap, ws);
+    if (st != LLB_OK) return st;
+    if (T > cache_cap) return fail(LLB_E_CAPACITY, "T=%d exceeds cache_cap=%d", T, cache_cap);
+    if (T > b->cfg.max_positions)
+        return fail(LLB_E_CAPACITY, "T=%d exceeds max_positions=%d", T, b->cfg.max_positions);
+    return run_block(b, x, y, B, T, 0, k_cache, v_cache, cache_cap, ws, ws_bytes,
+                     (hipStream_t)stream, false);
+}
+
+llb_status llb_block_decode(llb_block* b, const float* x, float* y, int32_t B, int32_t start_pos,
+                            void* k_cache, void* v_cache, int32_t cache_cap, void* ws,
+                            size_t ws_bytes, void* stream) {
+    llb_status st = check_call(b, x, y, B, 1, k_cache, v_cache, cache_cap, ws);
+    if (st != LLB_OK) return st;
+    if (start_pos < 0) return fail(LLB_E_INVALID, "start_pos must be >= 0");
+    if (start_pos + 1 > cache_cap)
+        return fail(LLB_E_CAPACITY, "start_pos+1=%d exceeds cache_cap=%d", start_pos + 1, cache_cap);
+    if (start_pos >= b->cfg.max_positions)
+        return fail(LLB_E_CAPACITY, "start_pos=%d >= max_positions=%d", start_pos,
+                    b->cfg.max_positions);
+    return run_block(b, x, y, B, 1, start_pos, k_cache, v_cache, cache_cap, ws, ws_bytes,
+                     (hipStream_t)stream, true);
+}
+
+llb_status llb_kv_append(const llb_block* b, void* k_cache, void* v_cache, int32_t B,
+                         int32_t cache_cap, int32_t start_pos, int32_t n_new, const void* k_new,
+                         const void* v_new, void* stream) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!k_cache || !v_cache || !k_new || !v_new) return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (B <= 0 || n_new < 0 || start_pos < 0 || cache_cap <= 0)
+        return fail(LLB_E_INVALID, "bad sizes");
+    if ((long)start_pos + n_new > cache_cap)
+        return fail(LLB_E_CAPACITY, "start_pos+n_new=%ld exceeds cache_cap=%d",
+                    (long)start_pos + n_new, cache_cap);
+    hipError_t e = llb::kv_append_launch(k_cache, v_cache, k_new, v_new, B, b->cfg.n_kv_heads,
+                                         cache_cap, start_pos, n_new, b->cfg.head_dim, b->es,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_append");
+    return LLB_OK;
+}
+
+llb_status llb_attention_prefill(const llb_block* b, const void* q, const void* k_cache,
+                                 const void* v_cache, void* o, int32_t B, int32_t T,
+                                 int32_t start_pos, int32_t cache_cap, void* stream) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!q || !k_cache || !v_cache || !o) return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (B <= 0 || T <= 0 || start_pos < 0 || cache_cap <= 0) return fail(LLB_E_INVALID, "bad sizes");
+    if ((long)start_pos + T > cache_cap)
+        return fail(LLB_E_CAPACITY, "start_pos+T exceeds cache_cap");
+    const llb_config& c = b->cfg;
+    llb::AttnArgs at{};
+    at.q = q; at.k_cache = k_cache; at.v_cache = v_cache; at.o = o; at.B = B; at.T = T;
+    at.pos0 = start_pos; at.cap = cache_cap; at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads;
+    at.hd = c.head_dim;
+    hipError_t e = c.wdtype == LLB_F32 ? llb::attn_f32_launch(at, (hipStream_t)stream)
+                                       : llb::attn_prefill_bf16_launch(at, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention prefill");
+    return LLB_OK;
+}
+
+size_t llb_attention_workspace_bytes(const llb_block* b, int32_t B, int32_t n_keys) {
+    if (!handle_ok(b) || B <= 0 || n_keys <= 0) return 0;
+    const llb_config& c = b->cfg;
+    if (c.wdtype == LLB_F32) return 256;
+    return align_up(llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys));
+}
+
+llb_status llb_attention_decode(const llb_block* b, const void* q, const void* k_cache,
+                                const void* v_cache, void* o, int32_t B, int32_t start_pos,
+                                int32_t cache_cap, void* ws, size_t ws_bytes, void* stream) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!q || !k_cache || !v_cache || !o || !ws) return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (B <= 0 || start_pos < 0 || cache_cap <= 0) return fail(LLB_E_INVALID, "bad sizes");
+    if (start_pos + 1 > cache_cap) return fail(LLB_E_CAPACITY, "start_pos+1 exceeds cache_cap");
+    const size_t need = llb_attention_workspace_bytes(b, B, start_pos + 1);
+    if (ws_bytes < need) return fail(LLB_E_INVALID, "workspace too small: %zu < %zu", ws_bytes, need);
+    const llb_config& c = b->cfg;
+    llb::AttnArgs at{};
+    at.q = q; at.k_cache = k_cache; at.v_cache = v_cache; at.o = o; at.B = B; at.T = 1;
+    at.pos0 = start_pos; at.cap = cache_cap; at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads;
+    at.hd = c.head_dim;
+    hipError_t e = c.wdtype == LLB_F32
+                       ? llb::attn_f32_launch(at, (hipStream_t)stream)
+                       : llb::attn_decode_bf16_launch(at, (float*)ws, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention decode");
+    return LLB_OK;
+}
+
+llb_status llb_block_set_stage_timing(llb_block* b, int32_t enable) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    b->timing = enable ? 1 : 0;
+    return LLB_OK;
+}
+
+llb_status llb_block_stage_times(llb_block* b, float* ms, int32_t* n_calls) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!ms || !n_calls) return fail(LLB_E_INVALID, "output pointer is NULL");
+    for (int i = 0; i < 5; ++i) ms[i] = 0.f;
+    const size_t calls = b->events_used / 6;
+    if (calls > 0) {
+        hipError_t e = hipEventSynchronize(b->events[b->events_used - 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        for (size_t c = 0; c < calls; ++c)
+            for (int i = 0; i < 5; ++i) {
+                float t = 0.f;
+                e = hipEventElapsedTime(&t, b->events[6 * c + i], b->events[6 * c + i + 1]);
+                if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+                ms[i] += t;
+            }
+    }
+    *n_calls = (int32_t)calls;
+    b->events_used = 0;
+    return LLB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Device-side helpers shared by the gfx950 kernels of the block library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define LLB_DEV __device__ __forceinline__
+
+LLB_DEV float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+LLB_DEV bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+LLB_DEV uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// 8 fp32 -> one MFMA bf16x8 operand (element 0 in the low half of word 0).
+LLB_DEV bf16x8 to_bf16x8(const float* v) {
+    uint4 u;
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]);
+    u.w = pack_bf16x2(v[6], v[7]);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+LLB_DEV bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+LLB_DEV void unpack_bf16x8(uint4 u, float* v) {
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+// D(32x32) += A(32x16) B(16x32); lane l supplies A row l%32 and B column l%32,
+// k-elements 8*(l/32)..+8.  D: lane l holds column l%32, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4.
+LLB_DEV f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) B(32x16); lane l supplies A row l%16 and B column l%16,
+// k-elements 8*(l/16)..+8.  D: lane l holds column l%16, register r holds row
+// 4*(l/16) + r.
+LLB_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+LLB_DEV float warp_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+LLB_DEV float warp_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+LLB_DEV float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// Inverse RMS of a row from its fp32 sum of squares (eps inside the square root).
+LLB_DEV float inv_rms(float sumsq, int n, float eps) {
+    return 1.0f / sqrtf(sumsq / (float)n + eps);
+}
+
+// Workgroup id -> tile id such that consecutive tile ids run on the same XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs; tiles that share
+// operand panels should share an XCD's L2.
+LLB_DEV int xcd_remap(int bid, int nblocks) {
+    constexpr int XCD = 8;
+    if (nblocks % XCD != 0) return bid;
+    return (bid % XCD) * (nblocks / XCD) + bid / XCD;
+}

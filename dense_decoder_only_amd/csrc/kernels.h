@@ -1,0 +1,81 @@
+// Internal interface between the host orchestrator (block.cpp) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llb {
+
+enum EpiKind : int { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+// What a projection does with its fp32 result C[m, n] (after the row's inverse
+// RMS is applied when the A operand was normalised).
+struct Epilogue {
+    int kind;
+    // EPI_QKV: columns [0, n_heads*hd) are Q, then K, then V (each head hd wide).
+    // Q and K are rotated (interleaved pairs, rope[pos][i] = (cos, sin)); Q goes to
+    // q_out [B, n_heads, T, hd], K/V to cache rows pos = pos0 + t of [B, n_kv, cap, hd].
+    void* q_out;
+    void* k_cache;
+    void* v_cache;
+    const float2* rope;
+    int T, pos0, cap, n_heads, n_kv, hd;
+    // EPI_RESID: out[m, n] = resid[m, n] + C[m, n]   (fp32, [M, N] row-major)
+    const float* resid;
+    float* out;
+    // EPI_SWIGLU: columns come in 64-wide groups [gate 32 | up 32]; feature
+    // f = group*32 + j gets u[m, f] = SiLU(C_gate) * C_up, u is [M, N/2].
+    void* u_out;
+};
+
+// C = A . W^T.  A: [M, K] row-major, fp32 when `norm` (then A is scaled by the
+// per-column gain and each row's inverse RMS over its K values) or wdtype;
+// W: [N, K] row-major, wdtype.
+struct GemmArgs {
+    const void* A;
+    const float* gain;
+    const void* W;
+    int M, N, K;
+    int norm;
+    float eps;
+    Epilogue epi;
+};
+
+// ---- bf16 MFMA projections -----------------------------------------------
+// Large-M projection (prefill): LDS-staged bf16 MFMA tiles.
+hipError_t gemm_bf16_launch(const GemmArgs& a, int tile_cfg, hipStream_t s);
+// Tile configurations available to gemm_bf16_launch: returns BM, BN, threads.
+void gemm_bf16_tile(int tile_cfg, int* bm, int* bn, int* threads);
+int gemm_bf16_num_tile_cfgs();
+
+// Small-M projection (decode, M <= 64): weight-streaming split-K; writes fp32
+// partials [splits][M][N] and per-split row sums of squares [splits][M] to ws,
+// then applies the epilogue in a second pass.
+size_t gemv_bf16_ws_bytes(int M, int N, int splits);
+int gemv_bf16_splits(int M, int N, int K);
+hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_t s);
+
+// ---- fp32 projections (SIMT) ----------------------------------------------
+hipError_t gemm_f32_launch(const GemmArgs& a, hipStream_t s);
+
+// ---- attention --------------------------------------------------------------
+struct AttnArgs {
+    const void* q;        // prefill: [B, n_heads, T, hd]; decode: [B, n_heads, hd]
+    const void* k_cache;  // [B, n_kv, cap, hd]
+    const void* v_cache;
+    void* o;              // [B, T, n_heads*hd]
+    int B, T, pos0, cap, n_heads, n_kv, hd;
+};
+hipError_t attn_prefill_bf16_launch(const AttnArgs& a, hipStream_t s);
+// Split-K decode attention + merge.  ws: attn_decode_ws_bytes(...) bytes.
+size_t attn_decode_ws_bytes(int B, int n_heads, int n_kv, int hd, int n_keys);
+hipError_t attn_decode_bf16_launch(const AttnArgs& a, float* ws, hipStream_t s);
+// Plain fp32 attention (prefill or decode, any T).
+hipError_t attn_f32_launch(const AttnArgs& a, hipStream_t s);
+
+// ---- cache helpers ---------------------------------------------------------
+hipError_t kv_append_launch(void* kc, void* vc, const void* kn, const void* vn, int B, int n_kv,
+                            int cap, int pos0, int n_new, int hd, int elem_bytes, hipStream_t s);
+
+}  // namespace llb

@@ -1,0 +1,228 @@
+"""Python binding of the C ABI in include/llb.h (argument marshalling only).
+
+Every function has the name of its C counterpart and forwards to it through
+ctypes; all compute runs in the HIP library.  Tensors are torch CUDA (ROCm)
+tensors; their data pointers and torch's current stream are handed over as
+plain pointers.  If the library is not built, loading fails loudly: there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libllb.so")
+
+LLB_OK = 0
+LLB_E_INVALID = -1
+LLB_E_UNSUPPORTED = -2
+LLB_E_CAPACITY = -3
+LLB_E_HIP = -4
+LLB_E_NOMEM = -5
+LLB_F32 = 0
+LLB_BF16 = 1
+
+STATUS_NAMES = {0: "LLB_OK", -1: "LLB_E_INVALID", -2: "LLB_E_UNSUPPORTED", -3: "LLB_E_CAPACITY",
+                -4: "LLB_E_HIP", -5: "LLB_E_NOMEM"}
+
+EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes",
+            "llb_block_prefill", "llb_block_decode", "llb_kv_append", "llb_attention_prefill",
+            "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
+            "llb_block_stage_times", "llb_last_error")
+
+STAGES = ("qkv", "attention", "o_proj", "gate_up", "down")
+
+
+class llb_config(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_float), ("rope_scaling", ctypes.c_int32),
+        ("rs_factor", ctypes.c_float), ("rs_low_freq_factor", ctypes.c_float),
+        ("rs_high_freq_factor", ctypes.c_float), ("rs_orig_max_pos", ctypes.c_int32),
+        ("max_positions", ctypes.c_int32), ("wdtype", ctypes.c_int32),
+    ]
+
+
+class llb_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+
+
+class LlbError(RuntimeError):
+    def __init__(self, status: int, what: str, msg: str):
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libllb.so once; raises if it is missing (no CPU fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP block library not built: {path} is missing "
+                           "(run `python -m dense_decoder_only_amd.build`)")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.llb_block_create.argtypes = [ctypes.POINTER(llb_config), ctypes.POINTER(llb_weights), vp,
+                                     ctypes.POINTER(vp)]
+    lib.llb_block_create.restype = ctypes.c_int
+    lib.llb_block_destroy.argtypes = [vp]
+    lib.llb_block_destroy.restype = ctypes.c_int
+    lib.llb_block_workspace_bytes.argtypes = [vp, i32, i32]
+    lib.llb_block_workspace_bytes.restype = sz
+    lib.llb_block_prefill.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, vp, sz, vp]
+    lib.llb_block_prefill.restype = ctypes.c_int
+    lib.llb_block_decode.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, vp, sz, vp]
+    lib.llb_block_decode.restype = ctypes.c_int
+    lib.llb_kv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.llb_kv_append.restype = ctypes.c_int
+    lib.llb_attention_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.llb_attention_prefill.restype = ctypes.c_int
+    lib.llb_attention_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, sz, vp]
+    lib.llb_attention_decode.restype = ctypes.c_int
+    lib.llb_attention_workspace_bytes.argtypes = [vp, i32, i32]
+    lib.llb_attention_workspace_bytes.restype = sz
+    lib.llb_block_set_stage_timing.argtypes = [vp, i32]
+    lib.llb_block_set_stage_timing.restype = ctypes.c_int
+    lib.llb_block_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    lib.llb_block_stage_times.restype = ctypes.c_int
+    lib.llb_last_error.argtypes = []
+    lib.llb_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def llb_last_error() -> str:
+    return load_library().llb_last_error().decode()
+
+
+def _check(status: int, what: str):
+    if status != LLB_OK:
+        raise LlbError(status, what, llb_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the block library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_config(shape, max_positions: int) -> llb_config:
+    """llb_config from an object with the block's hyper-parameters (d_model,
+    n_heads, n_kv_heads, head_dim, d_ff, eps, rope_theta, rope_scaling, rs_*,
+    dtype 'bf16' | 'f32')."""
+    return llb_config(
+        d_model=shape.d_model, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
+        head_dim=shape.head_dim, d_ff=shape.d_ff, eps=shape.eps, rope_theta=shape.rope_theta,
+        rope_scaling=1 if shape.rope_scaling else 0, rs_factor=shape.rs_factor,
+        rs_low_freq_factor=shape.rs_low_freq_factor, rs_high_freq_factor=shape.rs_high_freq_factor,
+        rs_orig_max_pos=shape.rs_orig_max_pos, max_positions=max_positions,
+        wdtype=LLB_BF16 if shape.dtype == "bf16" else LLB_F32)
+
+
+class Block:
+    """A created block handle (llb_block*).  Destroy with llb_block_destroy."""
+
+    def __init__(self, handle: int, cfg: llb_config):
+        self.handle = ctypes.c_void_p(handle)
+        self.cfg = cfg
+
+    @property
+    def ptr(self):
+        return self.handle
+
+
+def llb_block_create(cfg: llb_config, weights: Dict[str, torch.Tensor], stream=None) -> Block:
+    lib = load_library()
+    w = llb_weights(**{k: weights[k].data_ptr() for k in
+                       ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")})
+    for k, t in weights.items():
+        if not t.is_contiguous():
+            raise ValueError(f"weight {k} must be contiguous")
+    out = ctypes.c_void_p()
+    _check(lib.llb_block_create(ctypes.byref(cfg), ctypes.byref(w), _stream(stream), ctypes.byref(out)),
+           "llb_block_create")
+    return Block(out.value, cfg)
+
+
+def llb_block_destroy(blk: Block) -> None:
+    _check(load_library().llb_block_destroy(blk.handle), "llb_block_destroy")
+    blk.handle = ctypes.c_void_p(0)
+
+
+def llb_block_workspace_bytes(blk: Block, B: int, T: int) -> int:
+    return int(load_library().llb_block_workspace_bytes(blk.handle, B, T))
+
+
+def llb_block_prefill(blk: Block, x, y, B, T, k_cache, v_cache, cache_cap, ws, stream=None):
+    _check(load_library().llb_block_prefill(blk.handle, _ptr(x), _ptr(y), B, T, _ptr(k_cache),
+                                            _ptr(v_cache), cache_cap, _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream)), "llb_block_prefill")
+
+
+def llb_block_decode(blk: Block, x, y, B, start_pos, k_cache, v_cache, cache_cap, ws, stream=None):
+    _check(load_library().llb_block_decode(blk.handle, _ptr(x), _ptr(y), B, start_pos, _ptr(k_cache),
+                                           _ptr(v_cache), cache_cap, _ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream(stream)), "llb_block_decode")
+
+
+def llb_kv_append(blk: Block, k_cache, v_cache, B, cache_cap, start_pos, n_new, k_new, v_new,
+                  stream=None):
+    _check(load_library().llb_kv_append(blk.handle, _ptr(k_cache), _ptr(v_cache), B, cache_cap,
+                                        start_pos, n_new, _ptr(k_new), _ptr(v_new), _stream(stream)),
+           "llb_kv_append")
+
+
+def llb_attention_prefill(blk: Block, q, k_cache, v_cache, o, B, T, start_pos, cache_cap, stream=None):
+    _check(load_library().llb_attention_prefill(blk.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                _ptr(o), B, T, start_pos, cache_cap, _stream(stream)),
+           "llb_attention_prefill")
+
+
+def llb_attention_workspace_bytes(blk: Block, B: int, n_keys: int) -> int:
+    return int(load_library().llb_attention_workspace_bytes(blk.handle, B, n_keys))
+
+
+def llb_attention_decode(blk: Block, q, k_cache, v_cache, o, B, start_pos, cache_cap, ws, stream=None):
+    _check(load_library().llb_attention_decode(blk.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                               _ptr(o), B, start_pos, cache_cap, _ptr(ws),
+                                               ws.numel() * ws.element_size(), _stream(stream)),
+           "llb_attention_decode")
+
+
+def llb_block_set_stage_timing(blk: Block, enable: bool) -> None:
+    _check(load_library().llb_block_set_stage_timing(blk.handle, 1 if enable else 0),
+           "llb_block_set_stage_timing")
+
+
+def llb_block_stage_times(blk: Block):
+    """(summed milliseconds per stage as a dict, number of recorded calls)."""
+    ms = (ctypes.c_float * 5)()
+    n = ctypes.c_int32()
+    _check(load_library().llb_block_stage_times(blk.handle, ms, ctypes.byref(n)), "llb_block_stage_times")
+    return dict(zip(STAGES, [float(v) for v in ms])), int(n.value)
+
+
+def workspace(blk: Block, B: int, T: int, device="cuda") -> torch.Tensor:
+    """A uint8 device tensor of llb_block_workspace_bytes(B, T) bytes."""
+    n = llb_block_workspace_bytes(blk, B, T)
+    if n == 0:
+        raise ValueError("llb_block_workspace_bytes returned 0 (bad handle or sizes)")
+    return torch.empty(n, dtype=torch.uint8, device=device)

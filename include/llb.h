@@ -1,0 +1,178 @@
+/*
+ * llb.h -- C ABI of a Llama-3/3.1 dense decoder block on MI355X (gfx950).
+ *
+ * One block computes, per token (pre-norm residual block, "Llama 3.1 70B"
+ * LLM diagram tool, section "Transformer layer"):
+ *
+ *     h = x + Wo . Attn(RMSNorm(x; g1))
+ *     y = h + Wdown . (SiLU(Wgate . RMSNorm(h; g2)) * (Wup . RMSNorm(h; g2)))
+ *
+ * where Attn is causal grouped-query attention with interleaved-pair RoPE over a
+ * KV cache kept at n_kv_heads ("Llama 3 8B - Prepare Q, K, V", atlas.klimoza.dev:
+ * header shapes and "Explanation"; "How Llama 3.1 Generates the Next Token",
+ * section "RoPE").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named x, y, k_cache, v_cache, q, o, ws, k_new, v_new are DEVICE
+ *    pointers owned by the caller.  llb_config and llb_weights are host structs;
+ *    the pointers inside llb_weights are device pointers.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call except create/destroy only enqueues work on it and returns without
+ *    synchronising.
+ *  - Weights use nn.Linear's [out, in] row-major layout ("Llama 3 8B - Prepare
+ *    Q, K, V", layers.py excerpt: F.linear computes x A^T, so the weight is
+ *    stored transposed).  Their element type, the gains' and the KV cache's is
+ *    llb_config.wdtype (fp32 or bf16).  The residual stream x, h, y is always fp32.
+ *  - Activations are row-major: x, y are [B, T, d_model] fp32, contiguous.
+ *  - Caches are [B, n_kv_heads, cache_cap, head_dim] in wdtype; row p of a
+ *    sequence holds position p; cached keys are stored after RoPE.
+ *  - Errors: every argument check runs on the host before any launch.  A bad
+ *    argument returns LLB_E_INVALID, an unsupported shape LLB_E_UNSUPPORTED, a
+ *    position range beyond cache_cap or max_positions LLB_E_CAPACITY, a HIP
+ *    runtime failure LLB_E_HIP, a failed allocation LLB_E_NOMEM.  Nothing is
+ *    enqueued when a check fails.  llb_last_error() returns a thread-local
+ *    message for the last non-OK status of the calling thread.  Nothing throws.
+ *  - Determinism: identical inputs give bitwise-identical outputs (no float
+ *    atomics; split reductions are summed in a fixed order).
+ *  - A handle is immutable after create; calls on different streams are safe
+ *    when their caches and workspaces are distinct.
+ */
+#ifndef LLB_H
+#define LLB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LLB_OK = 0,
+    LLB_E_INVALID = -1,
+    LLB_E_UNSUPPORTED = -2,
+    LLB_E_CAPACITY = -3,
+    LLB_E_HIP = -4,
+    LLB_E_NOMEM = -5
+} llb_status;
+
+typedef enum { LLB_F32 = 0, LLB_BF16 = 1 } llb_dtype;
+
+/* Block hyper-parameters, named as on the pages ("Llama 3 8B - Prepare Q, K,
+ * V", sku_list excerpt: dim, n_heads, n_kv_heads, norm_eps, rope_theta,
+ * use_scaled_rope).  Requirements: n_heads % n_kv_heads == 0,
+ * n_heads / n_kv_heads <= 16, head_dim in {64, 128}, d_model and d_ff multiples
+ * of 64, max_positions >= 1.  bf16 blocks additionally need head_dim == 128,
+ * n_heads / n_kv_heads <= 8, d_model and d_ff multiples of 256 and an even
+ * n_heads (LLB_E_UNSUPPORTED otherwise). */
+typedef struct {
+    int32_t d_model;          /* residual width d */
+    int32_t n_heads;          /* query heads */
+    int32_t n_kv_heads;       /* key/value heads (GQA groups) */
+    int32_t head_dim;         /* per-head width */
+    int32_t d_ff;             /* SwiGLU hidden width */
+    float   eps;              /* RMSNorm epsilon, inside the square root (1e-5) */
+    float   rope_theta;       /* RoPE base (500000) */
+    int32_t rope_scaling;     /* 0: plain schedule; 1: llama3 long-context scaling */
+    float   rs_factor;        /* llama3 scaling: slow-down factor of low frequencies (8) */
+    float   rs_low_freq_factor;   /* (1) */
+    float   rs_high_freq_factor;  /* (4) */
+    int32_t rs_orig_max_pos;  /* original context length (8192) */
+    int32_t max_positions;    /* RoPE table length: every position used must be < this */
+    int32_t wdtype;           /* llb_dtype of weights, gains and KV cache */
+} llb_config;
+
+/* Device pointers to the caller's weights, [out, in] row-major, wdtype.
+ * attn_norm, ffn_norm: [d_model].  wq: [n_heads*head_dim, d_model].
+ * wk, wv: [n_kv_heads*head_dim, d_model].  wo: [d_model, n_heads*head_dim].
+ * w_gate, w_up: [d_ff, d_model].  w_down: [d_model, d_ff]. */
+typedef struct {
+    const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+} llb_weights;
+
+typedef struct llb_block llb_block;
+
+/* Creates a block: copies and repacks the weights into library-owned device
+ * memory, builds the RoPE cos/sin table for positions [0, max_positions)
+ * ("Llama 3 8B - Prepare Q, K, V", model.py precompute_freqs_cis: float32
+ * inverse frequencies and float32 position*frequency products; llama3 scaling
+ * per "How Llama 3.1 Generates the Next Token", section "RoPE"), and
+ * synchronises `stream`.  The caller may free its weight tensors afterwards.
+ * Uses the current HIP device. */
+llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* stream,
+                            llb_block** out);
+
+/* Frees the library-owned memory of a handle.  Waits for the device first.
+ * NULL is accepted.  A handle that was already destroyed is rejected. */
+llb_status llb_block_destroy(llb_block* blk);
+
+/* Bytes of device workspace that llb_block_prefill (B sequences of T tokens)
+ * and, when T == 1, llb_block_decode need.  0 on a bad handle or size. */
+size_t llb_block_workspace_bytes(const llb_block* blk, int32_t B, int32_t T);
+
+/* Prefill: T new tokens per sequence at positions 0..T-1 over an empty cache
+ * ("Llama 3.1 70B", "Transformer layer" and "Grouped-Query Attention": causal
+ * attention, each query sees itself and earlier positions).  Writes the
+ * rotated keys and the values of the T tokens to cache rows 0..T-1 and
+ * y = block(x).  x, y: [B, T, d_model] fp32 (y may alias x).
+ * Needs T <= cache_cap and T <= max_positions. */
+llb_status llb_block_prefill(llb_block* blk, const float* x, float* y, int32_t B, int32_t T,
+                             void* k_cache, void* v_cache, int32_t cache_cap,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Decode: one new token per sequence at position start_pos = P, attending to
+ * cache rows 0..P-1 plus its own key, L = P + 1 keys ("Llama 3 8B - Prepare Q,
+ * K, V", header: decode reads L = P + 1 keys).  Writes cache row P and
+ * y = block(x).  x, y: [B, 1, d_model] fp32 (y may alias x).
+ * Needs P + 1 <= cache_cap and P < max_positions. */
+llb_status llb_block_decode(llb_block* blk, const float* x, float* y, int32_t B, int32_t start_pos,
+                            void* k_cache, void* v_cache, int32_t cache_cap,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Copies k_new, v_new [B, n_kv_heads, n_new, head_dim] (wdtype) into cache
+ * rows start_pos..start_pos+n_new-1 of every sequence and KV head.  Used to
+ * seed caches.  Needs start_pos + n_new <= cache_cap. */
+llb_status llb_kv_append(const llb_block* blk, void* k_cache, void* v_cache, int32_t B,
+                         int32_t cache_cap, int32_t start_pos, int32_t n_new,
+                         const void* k_new, const void* v_new, void* stream);
+
+/* Attention alone, on the block's head layout and dtype (unit-level access to
+ * the kernels used inside prefill/decode).
+ * llb_attention_prefill: q [B, n_heads, T, head_dim] holds rotated queries at
+ *   positions start_pos..start_pos+T-1; keys/values are cache rows
+ *   0..start_pos+T-1; query t sees keys <= start_pos+t ("How Llama 3.1
+ *   Generates the Next Token", block notation: mask M is -inf for future
+ *   positions; score q.k/sqrt(head_dim)).  o: [B, T, n_heads*head_dim].
+ * llb_attention_decode: q [B, n_heads, head_dim], one query per sequence at
+ *   position start_pos reading keys 0..start_pos; o: [B, n_heads*head_dim];
+ *   needs ws of llb_attention_workspace_bytes(blk, B, start_pos + 1) bytes.
+ * Query head h reads KV head h / (n_heads / n_kv_heads).  All in wdtype. */
+llb_status llb_attention_prefill(const llb_block* blk, const void* q, const void* k_cache,
+                                 const void* v_cache, void* o, int32_t B, int32_t T,
+                                 int32_t start_pos, int32_t cache_cap, void* stream);
+llb_status llb_attention_decode(const llb_block* blk, const void* q, const void* k_cache,
+                                const void* v_cache, void* o, int32_t B, int32_t start_pos,
+                                int32_t cache_cap, void* ws, size_t ws_bytes, void* stream);
+size_t llb_attention_workspace_bytes(const llb_block* blk, int32_t B, int32_t n_keys);
+
+/* Measurement hook for benchmarking tools.  While enabled, every
+ * llb_block_prefill / llb_block_decode call on `blk` records HIP events on its
+ * stream before and after each of its five stages, in this order: QKV
+ * projection (with RMSNorm, RoPE and the cache write), attention, output
+ * projection (+ residual), gate/up projection (with RMSNorm and SiLU.up), down
+ * projection (+ residual).  llb_block_stage_times waits for the recorded
+ * events, writes the summed milliseconds of each stage to ms[0..4] and the
+ * number of recorded calls to *n_calls, and clears the record.  Disabled by
+ * default; enabling it costs one event record per stage boundary. */
+llb_status llb_block_set_stage_timing(llb_block* blk, int32_t enable);
+llb_status llb_block_stage_times(llb_block* blk, float* ms, int32_t* n_calls);
+
+/* Thread-local text describing the last non-OK status ("" if none). */
+const char* llb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLB_H */

@@ -1,0 +1,114 @@
+"""The C ABI library on the host: it loads, exports every symbol that
+include/llb.h declares, and rejects bad arguments before touching the GPU.
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dense_decoder_only_amd import llb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llb.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(llb.LIB_PATH),
+                                reason="libllb.so not built (python -m dense_decoder_only_amd.build)")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(llb_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    syms = declared_symbols()
+    for name in ("llb_block_create", "llb_block_prefill", "llb_block_decode", "llb_kv_append",
+                 "llb_block_destroy", "llb_block_workspace_bytes", "llb_last_error"):
+        assert name in syms
+    assert set(syms) == set(llb.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = llb.load_library()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_config_struct_layout():
+    # 14 four-byte fields, no padding: must match the C struct
+    assert ctypes.sizeof(llb.llb_config) == 56
+    assert ctypes.sizeof(llb.llb_weights) == 9 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def _cfg(**kw):
+    base = dict(d_model=512, n_heads=8, n_kv_heads=2, head_dim=64, d_ff=1408, eps=1e-5,
+                rope_theta=500000.0, rope_scaling=0, rs_factor=8.0, rs_low_freq_factor=1.0,
+                rs_high_freq_factor=4.0, rs_orig_max_pos=8192, max_positions=128,
+                wdtype=llb.LLB_F32)
+    base.update(kw)
+    return llb.llb_config(**base)
+
+
+def _create(cfg, weights_ok=True):
+    lib = llb.load_library()
+    w = llb.llb_weights(*([1] * 9 if weights_ok else [0] * 9))
+    out = ctypes.c_void_p(123)
+    st = lib.llb_block_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_kv_heads=3), llb.LLB_E_INVALID),             # 8 % 3 != 0
+    (dict(d_model=0), llb.LLB_E_INVALID),
+    (dict(max_positions=0), llb.LLB_E_INVALID),
+    (dict(wdtype=7), llb.LLB_E_INVALID),
+    (dict(rope_theta=0.5), llb.LLB_E_INVALID),
+    (dict(rope_scaling=1, rs_low_freq_factor=4.0, rs_high_freq_factor=1.0), llb.LLB_E_INVALID),
+    (dict(head_dim=96), llb.LLB_E_UNSUPPORTED),
+    (dict(d_ff=1400), llb.LLB_E_UNSUPPORTED),
+    (dict(n_heads=64, n_kv_heads=2), llb.LLB_E_UNSUPPORTED),   # group of 32
+    (dict(wdtype=llb.LLB_BF16), llb.LLB_E_UNSUPPORTED),        # bf16 needs head_dim 128
+    (dict(wdtype=llb.LLB_BF16, head_dim=128, n_heads=16, n_kv_heads=1), llb.LLB_E_UNSUPPORTED),
+])
+def test_create_rejects_bad_configs(kw, status):
+    st, out = _create(_cfg(**kw))
+    assert st == status
+    assert out is None
+    assert llb.llb_last_error() != ""
+
+
+def test_create_rejects_null_weights_and_null_out():
+    st, out = _create(_cfg(), weights_ok=False)
+    assert st == llb.LLB_E_INVALID and out is None
+    assert "weight" in llb.llb_last_error()
+    lib = llb.load_library()
+    w = llb.llb_weights(*([1] * 9))
+    assert lib.llb_block_create(ctypes.byref(_cfg()), ctypes.byref(w), None, None) == llb.LLB_E_INVALID
+
+
+def test_calls_on_bad_handles_fail_before_any_launch():
+    lib = llb.load_library()
+    assert lib.llb_block_destroy(None) == llb.LLB_OK
+    assert lib.llb_block_workspace_bytes(None, 1, 1) == 0
+    p = ctypes.c_void_p(1)
+    assert lib.llb_block_prefill(None, p, p, 1, 1, p, p, 8, p, 1 << 20, None) == llb.LLB_E_INVALID
+    assert "handle" in llb.llb_last_error()
+    assert lib.llb_block_decode(None, p, p, 1, 0, p, p, 8, p, 1 << 20, None) == llb.LLB_E_INVALID
+    assert lib.llb_kv_append(None, p, p, 1, 8, 0, 1, p, p, None) == llb.LLB_E_INVALID
+    assert lib.llb_attention_prefill(None, p, p, p, p, 1, 1, 0, 8, None) == llb.LLB_E_INVALID
+    assert lib.llb_attention_decode(None, p, p, p, p, 1, 0, 8, p, 1 << 20, None) == llb.LLB_E_INVALID
+    assert lib.llb_attention_workspace_bytes(None, 1, 1) == 0
+    # a fake handle (wrong magic) is rejected too
+    junk = (ctypes.c_uint64 * 64)()
+    assert lib.llb_block_prefill(ctypes.cast(junk, ctypes.c_void_p), p, p, 1, 1, p, p, 8, p, 1 << 20,
+                                 None) == llb.LLB_E_INVALID
+    assert lib.llb_block_destroy(ctypes.cast(junk, ctypes.c_void_p)) == llb.LLB_E_INVALID
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(llb, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        llb.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,265 @@
+"""Unit parity of the attention kernels (llb_attention_prefill / _decode) on
+seeded bf16 queries, keys and values, against the oracle's fp64 attention fed
+the same bf16 values.
+
+Bar, per element: |gpu - oracle| <= 2^-8 |o| + 2^-8 sum_n p_n |v_n| + 1e-3 rms(o).
+The output is stored in bf16 (half an ulp is 2^-8 of the value).  The prefill
+kernel also rounds each softmax weight to bf16 before the P.V product (2^-9
+relative per weight); with few visible keys these roundings do not average out
+and reach 2^-9 sum_n p_n |v_n|, which the oracle gives as its attention over |v|.
+
+Structured cases catch what random inputs hide: a dominant key must be
+returned exactly, zero scores must give the plain mean of the visible values
+(a dropped first key or an extra key moves it by one part in L), and rows
+beyond the last visible key hold a large sentinel.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from dense_decoder_only_amd import llb
+from gpu_util import bf16_err, note, rel_err, shape
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 4096.0
+
+
+def _block(G, Hkv=2, max_positions=8192):
+    shp = shape(d_model=256, n_heads=G * Hkv, n_kv_heads=Hkv, head_dim=128, d_ff=256)
+    w, _ = workloads.make_weights(shp, 0)
+    w = {k: v.cuda() for k, v in w.items()}
+    cfg = llb.make_config(shp, max_positions)
+    return shp, llb.llb_block_create(cfg, w), w
+
+
+def _rand(shape_, gen, scale=1.0):
+    return (torch.randn(shape_, generator=gen) * scale).to(torch.bfloat16)
+
+
+def _oracle_prefill(q, kc, vc, pos0, T):
+    B = q.shape[0]
+    out = []
+    for b in range(B):
+        o = oracle.attention(q[b], kc[b], vc[b], np.arange(pos0, pos0 + T), n_keys=pos0 + T)
+        out.append(o.transpose(1, 0, 2).reshape(T, -1))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("G,B,T,pos0", [
+    (4, 1, 1, 0), (4, 2, 31, 0), (4, 1, 64, 0), (4, 2, 100, 0), (4, 1, 300, 0),
+    (8, 1, 130, 0), (1, 2, 70, 0), (2, 1, 65, 0),
+    (4, 2, 50, 17), (8, 1, 33, 64), (4, 1, 1, 500),
+])
+def test_attention_prefill_random(G, B, T, pos0):
+    shp, blk, _ = _block(G)
+    try:
+        H, Hkv, hd = shp.n_heads, shp.n_kv_heads, 128
+        cap = workloads.cache_capacity(pos0 + T)
+        gen = torch.Generator().manual_seed(1000 + T + pos0 + G)
+        q = _rand((B, H, T, hd), gen)
+        kc = torch.full((B, Hkv, cap, hd), SENTINEL, dtype=torch.bfloat16)
+        vc = kc.clone()
+        kc[:, :, :pos0 + T] = _rand((B, Hkv, pos0 + T, hd), gen, 0.6)
+        vc[:, :, :pos0 + T] = _rand((B, Hkv, pos0 + T, hd), gen)
+        note(f"attn prefill G={G} B={B} T={T} pos0={pos0}")
+        o = torch.empty(B, T, H * hd, dtype=torch.bfloat16, device="cuda")
+        llb.llb_attention_prefill(blk, q.cuda(), kc.cuda(), vc.cuda(), o, B, T, pos0, cap)
+        ref = _oracle_prefill(q, kc, vc, pos0, T)
+        mag = _oracle_prefill(q, kc, vc.abs(), pos0, T)
+        e = bf16_err(o.cpu(), ref, c=1e-3, mag=mag)
+        note(f"  bf16 err {e:.3f} (max/rms {rel_err(o.cpu(), ref):.2e})")
+        assert e <= 1.0
+    finally:
+        llb.llb_block_destroy(blk)
+
+
+@pytest.mark.parametrize("shift,pos0,T", [(0, 0, 127), (1, 0, 127), (0, 200, 100), (1, 200, 100),
+                                           (1, 0, 64), (1, 31, 33)])
+def test_attention_prefill_structured_mask(shift, pos0, T):
+    """Key n is 4 * e_(n mod 128); the query at position p is c * e_((p + shift) mod 128)
+    with a score of 30 for a matching key and 0 otherwise.  shift=0: the query's
+    own key dominates (dropping the diagonal from the mask would show); shift=1:
+    the next, future key would dominate if the mask leaked it.  Softmax weights
+    are exactly 1 or ~e^-30, so only the bf16 output rounding remains."""
+    shp, blk, _ = _block(4)
+    try:
+        B, H, Hkv, hd = 1, shp.n_heads, 2, 128
+        cap = workloads.cache_capacity(pos0 + T)
+        gen = torch.Generator().manual_seed(77 + pos0 + T)
+        kc = torch.zeros(B, Hkv, cap, hd, dtype=torch.bfloat16)
+        for n in range(pos0 + T):
+            kc[:, :, n, n % 128] = 4.0
+        vc = _rand((B, Hkv, cap, hd), gen)
+        q = torch.zeros(B, H, T, hd, dtype=torch.bfloat16)
+        for t in range(T):
+            q[:, :, t, (pos0 + t + shift) % 128] = 30.0 * math.sqrt(hd) / 4.0
+        note(f"attn prefill structured shift={shift} pos0={pos0} T={T}")
+        o = torch.empty(B, T, H * hd, dtype=torch.bfloat16, device="cuda")
+        llb.llb_attention_prefill(blk, q.cuda(), kc.cuda(), vc.cuda(), o, B, T, pos0, cap)
+        ref = _oracle_prefill(q, kc, vc, pos0, T)
+        e = bf16_err(o.cpu(), ref, c=1e-3)
+        note(f"  bf16 err {e:.3f}")
+        assert e <= 1.0
+    finally:
+        llb.llb_block_destroy(blk)
+
+
+def _run_decode(blk, shp, q, kc, vc, P):
+    B = q.shape[0]
+    H, hd = shp.n_heads, 128
+    cap = kc.shape[2]
+    ws = torch.empty(llb.llb_attention_workspace_bytes(blk, B, P + 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, H * hd, dtype=torch.bfloat16, device="cuda")
+    llb.llb_attention_decode(blk, q.cuda(), kc.cuda(), vc.cuda(), o, B, P, cap, ws)
+    return o.cpu()
+
+
+def _oracle_decode(q, kc, vc, P):
+    out = []
+    for b in range(q.shape[0]):
+        o = oracle.attention(q[b][:, None, :], kc[b], vc[b], [P], n_keys=P + 1)
+        out.append(o[:, 0, :].reshape(-1))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("G,B,P", [
+    (4, 1, 0), (4, 3, 1), (4, 2, 14), (4, 2, 15), (4, 2, 16), (4, 32, 1000),
+    (8, 2, 4096), (1, 2, 200), (2, 3, 77), (8, 64, 129), (8, 1, 16383),
+])
+def test_attention_decode_random(G, B, P):
+    Hkv = 2
+    shp, blk, _ = _block(G, Hkv, max_positions=16384)
+    try:
+        H, hd = shp.n_heads, 128
+        cap = workloads.cache_capacity(P + 1)
+        gen = torch.Generator().manual_seed(2000 + P + G + B)
+        q = _rand((B, H, hd), gen)
+        kc = torch.full((B, Hkv, cap, hd), SENTINEL, dtype=torch.bfloat16)
+        vc = kc.clone()
+        kc[:, :, :P + 1] = _rand((B, Hkv, P + 1, hd), gen, 0.6)
+        vc[:, :, :P + 1] = _rand((B, Hkv, P + 1, hd), gen)
+        note(f"attn decode G={G} B={B} P={P}")
+        o = _run_decode(blk, shp, q, kc, vc, P)
+        ref = _oracle_decode(q, kc, vc, P)
+        mag = _oracle_decode(q, kc, vc.abs(), P)
+        e = bf16_err(o, ref, c=1e-3, mag=mag)
+        note(f"  bf16 err {e:.3f} (max/rms {rel_err(o, ref):.2e})")
+        assert e <= 1.0
+    finally:
+        llb.llb_block_destroy(blk)
+
+
+@pytest.mark.parametrize("P", [1, 63, 1000, 4096])
+def test_attention_decode_uniform_scores_give_mean_of_all_keys(P):
+    """q = 0: every visible key has score 0, so o = mean of the P + 1 values.
+    V row 0 carries a large marker: dropping key 0 (or reading one key more)
+    changes o[0] by about marker / (P + 1)."""
+    shp, blk, _ = _block(4)
+    try:
+        B, H, hd = 2, shp.n_heads, 128
+        cap = workloads.cache_capacity(P + 2)
+        q = torch.zeros(B, H, hd, dtype=torch.bfloat16)
+        kc = torch.zeros(B, 2, cap, hd, dtype=torch.bfloat16)
+        vc = torch.zeros(B, 2, cap, hd, dtype=torch.bfloat16)
+        vc[:, :, 0, 0] = 256.0          # first key's marker
+        vc[:, :, P, 1] = 256.0          # own (newest) key's marker
+        vc[:, :, P + 1, 2] = 256.0      # one past the end: must not be read
+        note(f"attn decode uniform P={P}")
+        o = _run_decode(blk, shp, q, kc, vc, P).float().view(B, H, hd)
+        expect = 256.0 / (P + 1)
+        assert torch.allclose(o[:, :, 0], torch.full_like(o[:, :, 0], expect), rtol=8e-3)
+        assert torch.allclose(o[:, :, 1], torch.full_like(o[:, :, 1], expect), rtol=8e-3)
+        assert torch.all(o[:, :, 2] == 0)
+    finally:
+        llb.llb_block_destroy(blk)
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+def test_attention_dominant_key_is_selected(mode):
+    """One key aligned with the query and 30 units of score above the rest: the
+    output is that key's value row, to bf16 precision."""
+    shp, blk, _ = _block(4)
+    try:
+        B, H, hd, Hkv = 1, shp.n_heads, 128, 2
+        P = 700
+        T = 1 if mode == "decode" else 40
+        pos0 = P if mode == "decode" else P - T + 1
+        cap = workloads.cache_capacity(P + 1)
+        gen = torch.Generator().manual_seed(3)
+        star = 123
+        kc = _rand((B, Hkv, cap, hd), gen, 0.05)
+        vc = _rand((B, Hkv, cap, hd), gen)
+        kc[:, :, star, :] = 0
+        kc[:, :, star, 0] = 4.0
+        q = torch.zeros(B, H, T, hd, dtype=torch.bfloat16)
+        q[..., 0] = 30.0 * math.sqrt(hd) / 4.0   # q.k_star / sqrt(hd) = 30
+        note(f"attn dominant key {mode}")
+        if mode == "decode":
+            o = _run_decode(blk, shp, q[:, :, 0], kc, vc, P).float().view(B, H, hd)
+            o = o[:, :, None, :]
+        else:
+            out = torch.empty(B, T, H * hd, dtype=torch.bfloat16, device="cuda")
+            llb.llb_attention_prefill(blk, q.cuda(), kc.cuda(), vc.cuda(), out, B, T, pos0, cap)
+            o = out.cpu().float().view(B, T, H, hd).permute(0, 2, 1, 3)
+        for h in range(H):
+            ref = vc[0, h // 4, star].float()
+            assert torch.allclose(o[0, h], ref.expand_as(o[0, h]), atol=2e-2, rtol=1e-2)
+    finally:
+        llb.llb_block_destroy(blk)
+
+
+def test_kv_append_is_exact():
+    shp, blk, _ = _block(4)
+    try:
+        B, Hkv, hd, cap = 3, 2, 128, 96
+        gen = torch.Generator().manual_seed(9)
+        kc = _rand((B, Hkv, cap, hd), gen).cuda()
+        vc = _rand((B, Hkv, cap, hd), gen).cuda()
+        k0, v0 = kc.cpu(), vc.cpu()
+        kn = _rand((B, Hkv, 20, hd), gen)
+        vn = _rand((B, Hkv, 20, hd), gen)
+        note("kv_append")
+        llb.llb_kv_append(blk, kc, vc, B, cap, 40, 20, kn.cuda(), vn.cuda())
+        k1, v1 = kc.cpu(), vc.cpu()
+        k0[:, :, 40:60] = kn
+        v0[:, :, 40:60] = vn
+        assert torch.equal(k1, k0) and torch.equal(v1, v0)
+        with pytest.raises(llb.LlbError) as ei:
+            llb.llb_kv_append(blk, kc, vc, B, cap, 90, 20, kn.cuda(), vn.cuda())
+        assert ei.value.status == llb.LLB_E_CAPACITY
+    finally:
+        llb.llb_block_destroy(blk)
+
+
+def test_capacity_and_workspace_errors():
+    shp, blk, _ = _block(4, max_positions=100)
+    try:
+        B, T = 1, 64
+        x = torch.zeros(B, T, 256, device="cuda")
+        y = torch.empty_like(x)
+        kc = torch.zeros(B, 2, 64, 128, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        ws = llb.workspace(blk, B, T)
+        note("error paths")
+        with pytest.raises(llb.LlbError) as ei:      # T > cap
+            llb.llb_block_prefill(blk, x, y, B, T, kc[:, :, :32].contiguous(), vc[:, :, :32].contiguous(), 32, ws)
+        assert ei.value.status == llb.LLB_E_CAPACITY
+        with pytest.raises(llb.LlbError) as ei:      # workspace too small
+            llb.llb_block_prefill(blk, x, y, B, T, kc, vc, 64, ws[: ws.numel() // 2])
+        assert ei.value.status == llb.LLB_E_INVALID
+        x1 = x[:, :1].contiguous()
+        ws1 = llb.workspace(blk, B, 1)
+        with pytest.raises(llb.LlbError) as ei:      # P + 1 > cap
+            llb.llb_block_decode(blk, x1, x1.clone(), B, 64, kc, vc, 64, ws1)
+        assert ei.value.status == llb.LLB_E_CAPACITY
+        big = torch.zeros(B, 2, 256, 128, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(llb.LlbError) as ei:      # beyond the RoPE table
+            llb.llb_block_decode(blk, x1, x1.clone(), B, 150, big, big.clone(), 256, ws1)
+        assert ei.value.status == llb.LLB_E_CAPACITY
+    finally:
+        llb.llb_block_destroy(blk)
