@@ -162,11 +162,12 @@ hipError_t stage_event(llb_block* b, hipStream_t s) {
 }
 
 struct WsPlan {
-    size_t q = 0, o = 0, h = 0, u = 0, scratch = 0, total = 0;
+    size_t q = 0, o = 0, h = 0, u = 0, a1 = 0, a2 = 0, ssq1 = 0, ssq2 = 0, scratch = 0, total = 0;
     size_t scratch_bytes = 0;
 };
 
-// Workspace layout for one call: Q_r, O, h, u, then a scratch area (split-K
+// Workspace layout for one call: Q_r, O, h, u, the two RMSNorm operands (bf16
+// x*g1 and h*g2) with their row sums of squares, then a scratch area (split-K
 // partials of the decode projections, decode-attention partials).
 WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
     const llb_config& c = b->cfg;
@@ -178,6 +179,12 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
     p.o = off; off += align_up(M * c.n_heads * c.head_dim * es);
     p.h = off; off += align_up(M * c.d_model * sizeof(float));
     p.u = off; off += align_up(M * c.d_ff * es);
+    if (c.wdtype == LLB_BF16) {
+        p.a1 = off; off += align_up(M * c.d_model * 2);
+        p.a2 = off; off += align_up(M * c.d_model * 2);
+        p.ssq1 = off; off += align_up(M * sizeof(float));
+        p.ssq2 = off; off += align_up(M * (size_t)(c.d_model / 128) * sizeof(float));
+    }
     p.scratch = off;
     size_t scratch = 0;
     if (decode && c.wdtype == LLB_BF16) {
@@ -226,8 +233,14 @@ int pick_tile(int M, int N) {
     return best;
 }
 
+// Prefill tile configuration of a bf16 projection (-1 if none fits N).
+int tile_for(const llb_block* b, int override_cfg, int M, int N) {
+    (void)b;
+    return override_cfg >= 0 ? override_cfg : pick_tile(M, N);
+}
+
 llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, float* scratch,
-                    int tile_override, hipStream_t s, const char* what) {
+                    int tile, hipStream_t s, const char* what) {
     hipError_t e;
     if (b->cfg.wdtype == LLB_F32) {
         e = llb::gemm_f32_launch(a, s);
@@ -235,16 +248,16 @@ llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, fl
         const int sp = llb::gemv_bf16_splits(a.M, a.N, a.K);
         e = llb::gemv_bf16_launch(a, sp, scratch, s);
     } else {
-        const int t = tile_override >= 0 ? tile_override : pick_tile(a.M, a.N);
-        if (t < 0) return fail(LLB_E_UNSUPPORTED, "%s: no tile fits N=%d", what, a.N);
-        e = llb::gemm_bf16_launch(a, t, s);
+        if (tile < 0) return fail(LLB_E_UNSUPPORTED, "%s: no tile fits N=%d", what, a.N);
+        e = llb::gemm_bf16_launch(a, tile, s);
     }
     if (e != hipSuccess) return hip_fail(e, what);
     return LLB_OK;
 }
 
 // The kernel sequence of one block call over M = B*T tokens at positions
-// pos0..pos0+T-1 ("Llama 3.1 70B", section "Transformer layer").
+// pos0..pos0+T-1 ("Llama 3.1 70B", section "Transformer layer"):
+//   h = x + Wo . Attn(RMSNorm(x)),  y = h + Wdown . SwiGLU(RMSNorm(h)).
 llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int pos0, void* kc,
                      void* vc, int cap, void* ws, size_t ws_bytes, hipStream_t s, bool decode) {
     const llb_config& c = b->cfg;
@@ -257,10 +270,16 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     void* o = w + p.o;
     float* h = (float*)(w + p.h);
     void* u = w + p.u;
+    void* a1 = w + p.a1;
+    void* a2 = w + p.a2;
+    float* ssq1 = (float*)(w + p.ssq1);
+    float* ssq2 = (float*)(w + p.ssq2);
     float* scratch = (float*)(w + p.scratch);
     const int M = B * T;
     const int d = c.d_model, hd = c.head_dim;
+    const bool bf16 = c.wdtype == LLB_BF16;
     const bool small_m = decode && M <= 64;
+    const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * hd;
 
     llb::Epilogue e{};
     e.rope = b->rope;
@@ -271,10 +290,17 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
 
     // 1. RMSNorm(x) . Wqkv^T, RoPE, Q -> workspace, K/V -> cache rows pos0..pos0+T-1
     llb::GemmArgs a{};
-    a.A = x; a.gain = b->g1; a.W = b->wqkv; a.M = M; a.N = (c.n_heads + 2 * c.n_kv_heads) * hd;
-    a.K = d; a.norm = 1; a.eps = c.eps;
+    a.W = b->wqkv; a.M = M; a.N = nqkv; a.K = d; a.eps = c.eps;
+    if (bf16) {
+        hipError_t ne = llb::norm_rows_launch(x, b->g1, a1, ssq1, M, d, s);
+        if (ne != hipSuccess) return hip_fail(ne, "attention RMSNorm");
+        a.A = a1; a.ssq_in = ssq1; a.ssq_count = 1;
+    } else {
+        a.A = x; a.gain = b->g1; a.norm = 1;
+    }
     a.epi = e; a.epi.kind = llb::EPI_QKV; a.epi.q_out = q; a.epi.k_cache = kc; a.epi.v_cache = vc;
-    llb_status st = run_proj(b, a, small_m, scratch, b->tile_qkv, s, "qkv projection");
+    llb_status st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_qkv, M, nqkv), s,
+                             "qkv projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -283,33 +309,52 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     at.q = q; at.k_cache = kc; at.v_cache = vc; at.o = o; at.B = B; at.T = T; at.pos0 = pos0;
     at.cap = cap; at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads; at.hd = hd;
     hipError_t he;
-    if (c.wdtype == LLB_F32) he = llb::attn_f32_launch(at, s);
+    if (!bf16) he = llb::attn_f32_launch(at, s);
     else if (decode) he = llb::attn_decode_bf16_launch(at, scratch, s);
     else he = llb::attn_prefill_bf16_launch(at, s);
     if (he != hipSuccess) return hip_fail(he, "attention");
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
-    // 3. h = x + O . Wo^T
+    // 3. h = x + O . Wo^T   (bf16: also the FFN RMSNorm's operand and row sums of h^2)
+    const int tile_o = tile_for(b, b->tile_o, M, d);
     a = llb::GemmArgs{};
-    a.A = o; a.W = b->wo; a.M = M; a.N = d; a.K = c.n_heads * hd; a.norm = 0; a.eps = c.eps;
-    a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = x; a.epi.out = h;
-    st = run_proj(b, a, small_m, scratch, b->tile_o, s, "output projection");
+    a.A = o; a.W = b->wo; a.M = M; a.N = d; a.K = c.n_heads * hd; a.eps = c.eps;
+    a.epi = e; a.epi.resid = x; a.epi.out = h;
+    int ssq2_count = 1;
+    if (bf16) {
+        a.epi.kind = llb::EPI_RESID_NORM; a.epi.gain = b->g2; a.epi.a_out = a2; a.epi.ssq_out = ssq2;
+        if (!small_m) {
+            if (tile_o < 0) return fail(LLB_E_UNSUPPORTED, "output projection: no tile fits N=%d", d);
+            int bm, bn, nt;
+            llb::gemm_bf16_tile(tile_o, &bm, &bn, &nt);
+            ssq2_count = d / bn;
+        }
+    } else {
+        a.epi.kind = llb::EPI_RESID;
+    }
+    st = run_proj(b, a, small_m, scratch, tile_o, s, "output projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
     // 4. u = SiLU(RMSNorm(h) . Wgate^T) * (RMSNorm(h) . Wup^T)
     a = llb::GemmArgs{};
-    a.A = h; a.gain = b->g2; a.W = b->wgu; a.M = M; a.N = 2 * c.d_ff; a.K = d; a.norm = 1;
-    a.eps = c.eps; a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
-    st = run_proj(b, a, small_m, scratch, b->tile_gu, s, "gate/up projection");
+    a.W = b->wgu; a.M = M; a.N = 2 * c.d_ff; a.K = d; a.eps = c.eps;
+    if (bf16) {
+        a.A = a2; a.ssq_in = ssq2; a.ssq_count = ssq2_count;
+    } else {
+        a.A = h; a.gain = b->g2; a.norm = 1;
+    }
+    a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
+    st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_gu, M, 2 * c.d_ff), s,
+                  "gate/up projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
     // 5. y = h + u . Wdown^T
     a = llb::GemmArgs{};
-    a.A = u; a.W = b->wdown; a.M = M; a.N = d; a.K = c.d_ff; a.norm = 0; a.eps = c.eps;
+    a.A = u; a.W = b->wdown; a.M = M; a.N = d; a.K = c.d_ff; a.eps = c.eps;
     a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = h; a.epi.out = y;
-    st = run_proj(b, a, small_m, scratch, b->tile_down, s, "down projection");
+    st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_down, M, d), s, "down projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
     return LLB_OK;

@@ -1,17 +1,26 @@
 // Large-M bf16 projection C = A . W^T on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
 //
-// Block tile BM x BN, K step 64, double-buffered LDS; both operands are
-// K-contiguous ([rows][K] row-major), so every MFMA fragment is one 16-byte LDS
-// read.  LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with
-// (row & 7) so that the 32 lanes reading one fragment column hit distinct banks.
+// Both operands are bf16 and K-contiguous ([rows][K] row-major).  Tiles of
+// BM x BK (A) and BN x BK (W) are copied global -> LDS by the DMA path of the
+// vector memory unit (global_load_lds_dwordx4: each lane's 16 bytes land in LDS
+// without passing through registers), STAGES k-tiles ahead of the MFMAs.  The
+// only synchronisation per k-tile is one `s_waitcnt vmcnt(n)` that retires the
+// oldest stage's copies and one workgroup barrier.
 //
-// NORM variant (RMSNorm fused into the prologue, "Llama 3.1 70B", section
-// "RMSNorm": y = x / sqrt(mean(x^2) + eps) * g, reduction in fp32): A is the fp32
-// residual stream.  While staging a tile the loader multiplies x by the gain,
-// rounds once to bf16 for the MFMA, and accumulates sum(x^2) of its rows in
-// fp32.  The K loop covers whole rows (K = d_model), so after the loop each
-// row's inverse RMS is known and is applied to the fp32 accumulators in the
-// epilogue: C = r_m * sum_k bf16(x_mk g_k) W_nk.
+// LDS rows are BK = 32 bf16 (64 bytes, four 16-byte chunks).  Chunk c of row r
+// is stored at chunk position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the
+// 32 lanes reading one MFMA fragment column (32 consecutive rows, one chunk)
+// spread over all banks for 32- and 64-bank LDS alike.  The DMA writes 1 KB per
+// wave instruction (16 rows); lane i fetches the global chunk that belongs at
+// its fixed LDS slot, which realises the swizzle for free.
+//
+// Epilogues (see epilogue.cuh) run on the fp32 accumulators:
+//   EPI_QKV        rows scaled by 1/rms(x) from the row-norm kernel's sum of
+//                  squares, RoPE, Q/K/V scattered to the query buffer and cache;
+//   EPI_RESID      out = resid + C;
+//   EPI_RESID_NORM out = h = resid + C, plus the operand of the next RMSNorm,
+//                  bf16(h * g), and this tile's partial sum of h^2 per row;
+//   EPI_SWIGLU     rows scaled by 1/rms(h) from those partials, SiLU(gate)*up.
 #include "common.cuh"
 #include "epilogue.cuh"
 #include "kernels.h"
@@ -20,106 +29,124 @@ namespace llb {
 
 namespace {
 
-constexpr int BK = 64;
+constexpr int BK = 32;
+constexpr int STAGES = 4;
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool NORM, int EPI>
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's
+// 16 bytes land at LDS byte address lds + 16 * i.  Issued from inline assembly
+// so that the compiler does not treat every later LDS read as depending on it
+// (it would otherwise wait for all copies in flight before each read); the
+// kernel retires the copies itself with s_waitcnt vmcnt.
+LLB_DEV void dma16(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
+LLB_DEV uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+LLB_DEV int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding, expcnt left at its maximum):
+// this wave's copies older than the n most recent have landed in LDS, and its
+// own LDS reads have completed.
+template <int N>
+LLB_DEV void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding DMA copy); the empty asm keeps the compiler from
+// moving LDS accesses across it.
+LLB_DEV void barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_bf16_kernel(GemmArgs args) {
-    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M;
     constexpr int WTN = BN / WAVES_N;
     constexpr int TM = WTM / 32;
     constexpr int TN = WTN / 32;
-    constexpr int A_PER_T = NORM ? (BM * 16) / NT : (BM * 8) / NT;  // 16-byte chunks per thread
-    constexpr int B_PER_T = (BN * 8) / NT;
-    static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small for the thread count");
+    constexpr int STAGE_ELEMS = (BM + BN) * BK;
+    constexpr int BLOCKS = (BM + BN) / 16;   // 1 KB DMA blocks per stage
+    constexpr int L = BLOCKS / NW;            // DMA instructions per wave per stage
+    static_assert(BLOCKS % NW == 0 && BM % 16 == 0, "DMA split");
+    static_assert(2 * L < 64, "vmcnt range");
     static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs in a wave");
 
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
-    __shared__ float sScale[NORM ? BM : 1];
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS];
+    __shared__ float sScale[BM];
+    __shared__ float sPart[(EPI == EPI_RESID_NORM) ? WAVES_N * BM : 1];
 
     const int M = args.M, N = args.N, K = args.K;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = N / BN;
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     const int m0 = (tile % tiles_m) * BM;
-    const int n0 = (tile / tiles_m) * BN;
+    const int tn = tile / tiles_m;
+    const int n0 = tn * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WAVES_M;
     const int wn = wave / WAVES_M;
 
+    const bf16_t* __restrict__ A = (const bf16_t*)args.A;
     const bf16_t* __restrict__ W = (const bf16_t*)args.W;
 
-    uint4 ra[A_PER_T];
-    uint4 rb[B_PER_T];
-    float4 rg = make_float4(0.f, 0.f, 0.f, 0.f);
-    float ssq[NORM ? A_PER_T : 1];
+    // Per-lane global source of each of this wave's DMA blocks (k0 = 0).
+    const bf16_t* src[L];
 #pragma unroll
-    for (int i = 0; i < (NORM ? A_PER_T : 1); ++i) ssq[i] = 0.f;
-
-    auto load_tile = [&](int kt) {
-        const int k0 = kt * BK;
-        if constexpr (NORM) {
-            const float* __restrict__ A = (const float*)args.A;
-            const int c4 = tid & 15;
-            rg = *(const float4*)(args.gain + k0 + c4 * 4);
-#pragma unroll
-            for (int i = 0; i < A_PER_T; ++i) {
-                const int gm = m0 + (tid >> 4) + i * (NT / 16);
-                ra[i] = gm < M ? *(const uint4*)(A + (size_t)gm * K + k0 + c4 * 4)
-                               : make_uint4(0, 0, 0, 0);
-            }
+    for (int i = 0; i < L; ++i) {
+        const int blk = wave + i * NW;
+        const int row = blk * 16 + (lane >> 2);          // row in the [A; W] stage
+        const int chunk = (lane & 3) ^ swz(row);
+        if (blk * 16 < BM) {
+            const int gm = min(m0 + row, M - 1);         // rows past M: any valid row
+            src[i] = A + (size_t)gm * K + chunk * 8;
         } else {
-            const bf16_t* __restrict__ A = (const bf16_t*)args.A;
-            const int c8 = tid & 7;
-#pragma unroll
-            for (int i = 0; i < A_PER_T; ++i) {
-                const int gm = m0 + (tid >> 3) + i * (NT / 8);
-                ra[i] = gm < M ? *(const uint4*)(A + (size_t)gm * K + k0 + c8 * 8)
-                               : make_uint4(0, 0, 0, 0);
-            }
+            src[i] = W + (size_t)(n0 + row - BM) * K + chunk * 8;
         }
-        const int c8 = tid & 7;
+    }
+    // Copies of k-tile kt into stage `st` (a compile-time constant at every call:
+    // the stage offsets must be constants for the compiler to see that the LDS
+    // reads of one stage do not depend on the copies in flight to another).
+    const uint32_t lds_base = lds_offset(smem);
+    auto issue = [&](int kt, int st) {
 #pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            const int row = (tid >> 3) + i * (NT / 8);
-            rb[i] = *(const uint4*)(W + (size_t)(n0 + row) * K + k0 + c8 * 8);
+        for (int i = 0; i < L; ++i) {
+            const int blk = wave + i * NW;
+            dma16(src[i] + kt * BK,
+                  lds_base + (uint32_t)((st * STAGE_ELEMS + blk * 16 * BK) * sizeof(bf16_t)));
         }
     };
 
-    auto store_tile = [&](int buf) {
-        if constexpr (NORM) {
-            const int c4 = tid & 15;
-            const int c = c4 >> 1, half = c4 & 1;
-#pragma unroll
-            for (int i = 0; i < A_PER_T; ++i) {
-                const int row = (tid >> 4) + i * (NT / 16);
-                const float4 v = __builtin_bit_cast(float4, ra[i]);
-                ssq[i] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-                uint2 p;
-                p.x = pack_bf16x2(v.x * rg.x, v.y * rg.y);
-                p.y = pack_bf16x2(v.z * rg.z, v.w * rg.w);
-                *(uint2*)&sA[buf][row * BK + ((c ^ (row & 7)) << 3) + (half << 2)] = p;
-            }
-        } else {
-            const int c = tid & 7;
-#pragma unroll
-            for (int i = 0; i < A_PER_T; ++i) {
-                const int row = (tid >> 3) + i * (NT / 8);
-                *(uint4*)&sA[buf][row * BK + ((c ^ (row & 7)) << 3)] = ra[i];
-            }
+    // row scales for the normalised-operand epilogues (before the first copies
+    // are issued, so that waiting for these loads does not drain the pipeline)
+    if constexpr (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
+        for (int i = tid; i < BM; i += 64 * NW) {
+            const int m = m0 + i;
+            float s = 0.f;
+            if (m < M)
+                for (int p = 0; p < args.ssq_count; ++p) s += args.ssq_in[(size_t)p * M + m];
+            sScale[i] = inv_rms(s, K, args.eps);
         }
-        const int c = tid & 7;
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            const int row = (tid >> 3) + i * (NT / 8);
-            *(uint4*)&sB[buf][row * BK + ((c ^ (row & 7)) << 3)] = rb[i];
-        }
-    };
+    }
+
+    const int nk = K / BK;
+    static_assert(STAGES == 4, "the main loop below is unrolled over 4 stages");
+    if (0 < nk) issue(0, 0);
+    if (1 < nk) issue(1, 1);
+    if (2 < nk) issue(2, 2);
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -129,22 +156,22 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    auto compute = [&](int buf) {
-        const bf16_t* a_s = sA[buf];
-        const bf16_t* b_s = sB[buf];
+    auto compute = [&](int st) {
+        const bf16_t* a_s = smem + st * STAGE_ELEMS;
+        const bf16_t* b_s = a_s + BM * BK;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = kk * 2 + (lane >> 5);
+            const int c = 2 * kk + (lane >> 5);
             bf16x8 af[TM], bfr[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int r = wm * WTM + i * 32 + (lane & 31);
-                af[i] = as_bf16x8(*(const uint4*)&a_s[r * BK + ((c ^ (r & 7)) << 3)]);
+                af[i] = as_bf16x8(*(const uint4*)&a_s[r * BK + ((c ^ swz(r)) << 3)]);
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int r = wn * WTN + j * 32 + (lane & 31);
-                bfr[j] = as_bf16x8(*(const uint4*)&b_s[r * BK + ((c ^ (r & 7)) << 3)]);
+                bfr[j] = as_bf16x8(*(const uint4*)&b_s[r * BK + ((c ^ swz(r)) << 3)]);
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -152,61 +179,100 @@ gemm_bf16_kernel(GemmArgs args) {
                 for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
     };
-
-    const int nk = K / BK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load_tile(kt + 1);
-        compute(cur);
-        if (kt + 1 < nk) store_tile(cur ^ 1);
-        __syncthreads();
+    // One k-tile: retire its copies (later ones stay in flight), barrier, refill
+    // the stage that was read one step earlier, multiply.
+    auto step = [&](int kt, int rd, int wr) {
+        if (kt + 2 < nk) wait_vm_lgkm<2 * L>();
+        else if (kt + 1 < nk) wait_vm_lgkm<L>();
+        else wait_vm_lgkm<0>();
+        barrier();
+        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, wr);
+        compute(rd);
+    };
+    for (int kt = 0; kt < nk; kt += 4) {
+        step(kt, 0, 3);
+        if (kt + 1 < nk) step(kt + 1, 1, 0);
+        if (kt + 2 < nk) step(kt + 2, 2, 1);
+        if (kt + 3 < nk) step(kt + 3, 3, 2);
     }
+    __syncthreads();  // no copies are in flight here; orders the sScale writes too
 
-    if constexpr (NORM) {
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            float s = ssq[i];
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            s += __shfl_xor(s, 4, 64);
-            s += __shfl_xor(s, 8, 64);
-            if ((tid & 15) == 0) sScale[(tid >> 4) + i * (NT / 16)] = inv_rms(s, K, args.eps);
-        }
-        __syncthreads();
-    }
-
+    // ---- epilogue: each 32-row slice of a wave's tile goes through LDS so that a
+    // lane owns 8 consecutive columns of a row (RoPE pairs and gate/up pairs in
+    // one thread, 16-byte stores).
     const Epilogue& e = args.epi;
+    constexpr int SROW = WTN + 4;                 // padded fp32 row of the staging slice
+    static_assert(4 * 32 * SROW * 4 <= STAGES * STAGE_ELEMS * 2, "staging fits in the stages");
+    float* stile = (float*)smem + wave * (32 * SROW);
+    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+        const int rbase = wm * WTM + i * 32;      // tile row of the slice's first row
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int rl = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int m = m0 + rl;
-            const float sc = NORM ? sScale[rl] : 1.0f;
-            if constexpr (EPI == EPI_SWIGLU) {
+            const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const float sc = SCALED ? sScale[rbase + rr] : 1.0f;
 #pragma unroll
-                for (int j = 0; j < TN; j += 2) {
-                    const float g = acc[i][j][r] * sc;
-                    const float u = acc[i][j + 1][r] * sc;
-                    const int ng = n0 + wn * WTN + j * 32;  // multiple of 64
-                    const int f = (ng >> 1) + (lane & 31);
-                    if (m < M) epi_swiglu<bf16_t>(e, m, f, N >> 1, g, u);
-                }
-            } else {
+            for (int j = 0; j < TN; ++j) stile[rr * SROW + j * 32 + (lane & 31)] = acc[i][j][r] * sc;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if constexpr (EPI == EPI_SWIGLU) {
+            constexpr int CPR = WTN / 16;         // (gate, up) chunk pairs per row
+            for (int idx = lane; idx < 32 * CPR; idx += 64) {
+                const int row = idx / CPR, ch = idx % CPR;
+                const int cg = (ch >> 2) * 64 + (ch & 3) * 8;   // gate columns in the slice
+                const int m = m0 + rbase + row;
+                float g[8], u[8];
+                *(float4*)&g[0] = *(const float4*)&stile[row * SROW + cg];
+                *(float4*)&g[4] = *(const float4*)&stile[row * SROW + cg + 4];
+                *(float4*)&u[0] = *(const float4*)&stile[row * SROW + cg + 32];
+                *(float4*)&u[4] = *(const float4*)&stile[row * SROW + cg + 36];
+                const int f = ((n0 + wn * WTN + cg - (cg & 63)) >> 1) + (cg & 63);
+                if (m < M) epi_swiglu8(e, m, f, N >> 1, g, u);
+            }
+        } else {
+            constexpr int CPR = WTN / 8;          // 8-column chunks per row
+            for (int idx = lane; idx < 32 * CPR; idx += 64) {
+                const int row = idx / CPR, ch = idx % CPR;
+                const int m = m0 + rbase + row;
+                const int n = n0 + wn * WTN + ch * 8;
+                float v[8];
+                *(float4*)&v[0] = *(const float4*)&stile[row * SROW + ch * 8];
+                *(float4*)&v[4] = *(const float4*)&stile[row * SROW + ch * 8 + 4];
+                if constexpr (EPI == EPI_QKV) {
+                    if (m < M) epi_qkv8(e, m, n, v);
+                } else {
+                    float ss = 0.f;
+                    if (m < M) {
+                        epi_resid8(e, m, n, N, v);
+                        if constexpr (EPI == EPI_RESID_NORM) ss = epi_norm_operand8(e, m, n, N, v);
+                    }
+                    if constexpr (EPI == EPI_RESID_NORM) {
+                        // the CPR lanes of one row are consecutive: reduce over them
+                        static_assert(CPR == 16 || CPR == 8, "row reduction width");
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int n = n0 + wn * WTN + j * 32 + (lane & 31);
-                    const float v = acc[i][j][r] * sc;
-                    if constexpr (EPI == EPI_QKV) {
-                        const float partner = __shfl_xor(v, 1, 64);
-                        if (m < M) epi_qkv<bf16_t>(e, m, n, v, partner);
-                    } else {
-                        if (m < M) epi_resid(e, m, n, N, v);
+                        for (int off = 1; off < CPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                        if ((lane % CPR) == 0) sPart[wn * BM + rbase + row] = ss;
                     }
                 }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    if constexpr (EPI == EPI_RESID_NORM) {
+        __syncthreads();
+        for (int rl = tid; rl < BM; rl += 64 * NW) {
+            const int m = m0 + rl;
+            if (m < M) {
+                float s = 0.f;
+#pragma unroll
+                for (int w = 0; w < WAVES_N; ++w) s += sPart[w * BM + rl];
+                e.ssq_out[(size_t)tn * M + m] = s;
             }
         }
     }
@@ -216,27 +282,29 @@ struct TileCfg {
     int bm, bn, wm, wn;
 };
 constexpr TileCfg kTiles[] = {
-    {256, 256, 2, 4},  // 8 waves, wave tile 128x64
-    {256, 128, 4, 2},  // 8 waves, wave tile 64x64
+    {256, 256, 2, 2},  // 4 waves, wave tile 128x128
+    {256, 128, 2, 2},  // 4 waves, wave tile 128x64
     {128, 128, 2, 2},  // 4 waves, wave tile 64x64
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int BM, int BN, int WM, int WN, bool NORM, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NORM, EPI>), dim3(tiles),
-                       dim3(64 * WM * WN), 0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(tiles), dim3(64 * WM * WN),
+                       0, s, a);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-    const int kind = a.epi.kind;
-    if (kind == EPI_QKV && a.norm) return launch_one<BM, BN, WM, WN, true, EPI_QKV>(a, s);
-    if (kind == EPI_SWIGLU && a.norm) return launch_one<BM, BN, WM, WN, true, EPI_SWIGLU>(a, s);
-    if (kind == EPI_RESID && !a.norm) return launch_one<BM, BN, WM, WN, false, EPI_RESID>(a, s);
-    return hipErrorInvalidValue;
+    switch (a.epi.kind) {
+        case EPI_QKV: return launch_one<BM, BN, WM, WN, EPI_QKV>(a, s);
+        case EPI_SWIGLU: return launch_one<BM, BN, WM, WN, EPI_SWIGLU>(a, s);
+        case EPI_RESID: return launch_one<BM, BN, WM, WN, EPI_RESID>(a, s);
+        case EPI_RESID_NORM: return launch_one<BM, BN, WM, WN, EPI_RESID_NORM>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -252,10 +320,10 @@ void gemm_bf16_tile(int cfg, int* bm, int* bn, int* threads) {
 hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
     if (cfg < 0 || cfg >= kNumTiles) return hipErrorInvalidValue;
     const TileCfg t = kTiles[cfg];
-    if (a.M <= 0 || a.N % t.bn != 0 || a.K % BK != 0) return hipErrorInvalidValue;
+    if (a.M <= 0 || a.N % t.bn != 0 || a.K % BK != 0 || a.K / BK < 1) return hipErrorInvalidValue;
     switch (cfg) {
-        case 0: return launch_cfg<256, 256, 2, 4>(a, s);
-        case 1: return launch_cfg<256, 128, 4, 2>(a, s);
+        case 0: return launch_cfg<256, 256, 2, 2>(a, s);
+        case 1: return launch_cfg<256, 128, 2, 2>(a, s);
         default: return launch_cfg<128, 128, 2, 2>(a, s);
     }
 }

@@ -4,15 +4,13 @@
 // weight bytes over HBM bandwidth.  Each workgroup streams a 64-row x KS slab
 // of W straight from global memory into MFMA operand registers (W rows are
 // K-contiguous, so a 32x32x16 fragment is one 16-byte load per lane); the
-// token fragments come from L2 (the activations are a few hundred KB).  The 4
-// waves of a workgroup split the slab's K range and are summed through LDS;
-// workgroups along grid.y split K further and write fp32 partials, which a
-// second kernel sums in a fixed order and passes through the epilogue.
-//
-// NORM variant: A is the fp32 residual stream; tokens are multiplied by the
-// gain and rounded once to bf16 for the MFMA, and each split also emits its
-// rows' partial sum of squares so the epilogue can apply the inverse RMS
-// ("Llama 3.1 70B", section "RMSNorm", fp32 reduction).
+// token fragments (bf16, a few hundred KB in total) come from L2.  Per wave the
+// loads of one 64-wide k step are issued in the order [tokens(it), W(it + 1)],
+// so the wait for this step's operands leaves the next step's weights in
+// flight.  The 4 waves of a workgroup split the slab's K range and are summed
+// through LDS; workgroups along grid.y split K further and write fp32
+// partials, which a second kernel sums in split order and passes through the
+// epilogue.
 #include "common.cuh"
 #include "epilogue.cuh"
 #include "kernels.h"
@@ -22,15 +20,15 @@ namespace llb {
 namespace {
 
 constexpr int GV_ROWS = 64;    // W rows per workgroup
-constexpr int GV_UNROLL = 4;   // k-steps of 16 in flight per wave
+constexpr int GV_UNROLL = 4;   // k-steps of 16 per pipeline step (64 k)
 constexpr int GV_KQUANT = 4 * 16 * GV_UNROLL;  // K granularity of one split (256)
 
-template <int MT, bool NORM>
+template <int MT>
 __global__ void __launch_bounds__(256)
-gemv_bf16_kernel(GemmArgs args, int KS, float* __restrict__ part, float* __restrict__ stats) {
+gemv_bf16_kernel(GemmArgs args, int KS, float* __restrict__ part) {
     constexpr int MS = MT / 32;
+    constexpr int U = GV_UNROLL;
     __shared__ float sRed[4][MT * GV_ROWS];
-    __shared__ float sSsq[4][MT];
 
     const int M = args.M, N = args.N, K = args.K;
     const int n0 = blockIdx.x * GV_ROWS;
@@ -40,10 +38,20 @@ gemv_bf16_kernel(GemmArgs args, int KS, float* __restrict__ part, float* __restr
     const int KW = KS / 4;
     const int kw0 = split * KS + wave * KW;
     const int kl = 8 * (lane >> 5);
+    const int n_it = KW / (16 * U);
 
     const bf16_t* __restrict__ W = (const bf16_t*)args.W;
-    const bf16_t* wrow0 = W + (size_t)(n0 + (lane & 31)) * K + kl;
+    const bf16_t* __restrict__ A = (const bf16_t*)args.A;
+    const bf16_t* wrow0 = W + (size_t)(n0 + (lane & 31)) * K + kw0 + kl;
     const bf16_t* wrow1 = wrow0 + (size_t)32 * K;
+    const bf16_t* arow[MS];
+    bool tok_ok[MS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+        const int tok = ms * 32 + (lane & 31);
+        tok_ok[ms] = tok < M;
+        arow[ms] = A + (size_t)(tok_ok[ms] ? tok : 0) * K + kw0 + kl;
+    }
 
     f32x16 acc[MS][2];
 #pragma unroll
@@ -52,52 +60,46 @@ gemv_bf16_kernel(GemmArgs args, int KS, float* __restrict__ part, float* __restr
         for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[ms][ns][r] = 0.f;
-    float ssq[MS];
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms) ssq[ms] = 0.f;
 
-    for (int k = kw0; k < kw0 + KW; k += 16 * GV_UNROLL) {
-        uint4 wf[GV_UNROLL][2];
+    uint4 wa[U][2], wb[U][2];
+    auto load_w = [&](uint4 (&w)[U][2], int it) {
+        const int k = it * 16 * U;
 #pragma unroll
-        for (int u = 0; u < GV_UNROLL; ++u) {
-            wf[u][0] = *(const uint4*)(wrow0 + k + 16 * u);
-            wf[u][1] = *(const uint4*)(wrow1 + k + 16 * u);
+        for (int u = 0; u < U; ++u) {
+            w[u][0] = *(const uint4*)(wrow0 + k + 16 * u);
+            w[u][1] = *(const uint4*)(wrow1 + k + 16 * u);
         }
-        bf16x8 af[GV_UNROLL][MS];
+    };
+    auto load_a = [&](bf16x8 (&af)[U][MS], int it) {
+        const int k = it * 16 * U;
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-            const int tok = ms * 32 + (lane & 31);
+        for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-            for (int u = 0; u < GV_UNROLL; ++u) {
-                const int kk = k + 16 * u + kl;
-                if (tok < M) {
-                    if constexpr (NORM) {
-                        const float* xr = (const float*)args.A + (size_t)tok * K + kk;
-                        const float4 x0 = *(const float4*)xr;
-                        const float4 x1 = *(const float4*)(xr + 4);
-                        const float4 g0 = *(const float4*)(args.gain + kk);
-                        const float4 g1 = *(const float4*)(args.gain + kk + 4);
-                        ssq[ms] += x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w +
-                                   x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
-                        const float v[8] = {x0.x * g0.x, x0.y * g0.y, x0.z * g0.z, x0.w * g0.w,
-                                            x1.x * g1.x, x1.y * g1.y, x1.z * g1.z, x1.w * g1.w};
-                        af[u][ms] = to_bf16x8(v);
-                    } else {
-                        af[u][ms] = as_bf16x8(
-                            *(const uint4*)((const bf16_t*)args.A + (size_t)tok * K + kk));
-                    }
-                } else {
-                    af[u][ms] = as_bf16x8(make_uint4(0, 0, 0, 0));
-                }
-            }
-        }
+            for (int u = 0; u < U; ++u)
+                af[u][ms] = as_bf16x8(tok_ok[ms] ? *(const uint4*)(arow[ms] + k + 16 * u)
+                                                 : make_uint4(0, 0, 0, 0));
+    };
+    auto mma = [&](const uint4 (&w)[U][2], const bf16x8 (&af)[U][MS]) {
 #pragma unroll
-        for (int u = 0; u < GV_UNROLL; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
                 for (int ns = 0; ns < 2; ++ns)
-                    acc[ms][ns] = mfma32(af[u][ms], as_bf16x8(wf[u][ns]), acc[ms][ns]);
+                    acc[ms][ns] = mfma32(af[u][ms], as_bf16x8(w[u][ns]), acc[ms][ns]);
+    };
+
+    load_w(wa, 0);
+    for (int it = 0; it < n_it; it += 2) {
+        bf16x8 af[U][MS];
+        load_a(af, it);
+        if (it + 1 < n_it) load_w(wb, it + 1);
+        mma(wa, af);
+        if (it + 1 < n_it) {
+            load_a(af, it + 1);
+            if (it + 2 < n_it) load_w(wa, it + 2);
+            mma(wb, af);
+        }
     }
 
     // acc[ms][ns]: lane -> W row n0 + 32*ns + (lane & 31); reg r -> token
@@ -111,15 +113,7 @@ gemv_bf16_kernel(GemmArgs args, int KS, float* __restrict__ part, float* __restr
                 const int tok = ms * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 sRed[wave][tok * GV_ROWS + ns * 32 + (lane & 31)] = acc[ms][ns][r];
             }
-    if constexpr (NORM) {
-#pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-            const float s = ssq[ms] + __shfl_xor(ssq[ms], 32, 64);
-            if (lane < 32) sSsq[wave][ms * 32 + lane] = s;
-        }
-    }
     __syncthreads();
-
     for (int e = threadIdx.x; e < MT * GV_ROWS; e += 256) {
         const int tok = e / GV_ROWS;
         const int nl = e % GV_ROWS;
@@ -128,33 +122,27 @@ gemv_bf16_kernel(GemmArgs args, int KS, float* __restrict__ part, float* __restr
             part[((size_t)split * M + tok) * N + n0 + nl] = v;
         }
     }
-    if constexpr (NORM) {
-        if (blockIdx.x == 0 && threadIdx.x < M) {
-            const int t = threadIdx.x;
-            stats[(size_t)split * M + t] = (sSsq[0][t] + sSsq[1][t]) + (sSsq[2][t] + sSsq[3][t]);
-        }
-    }
 }
 
-// Sums the split partials in split order, applies the row's inverse RMS (NORM)
-// and the epilogue.  One thread per RoPE pair (QKV), output (RESID) or SwiGLU
-// feature (SWIGLU).
-template <int EPI, bool NORM>
+LLB_DEV float row_scale(const GemmArgs& a, int m) {
+    float s = 0.f;
+    for (int p = 0; p < a.ssq_count; ++p) s += a.ssq_in[(size_t)p * a.M + m];
+    return inv_rms(s, a.K, a.eps);
+}
+
+// Sums the split partials in split order, applies the row's inverse RMS (QKV,
+// SwiGLU) and the epilogue.  One thread per RoPE pair (QKV), output (RESID) or
+// SwiGLU feature (SWIGLU).
+template <int EPI>
 __global__ void __launch_bounds__(256)
-splitk_epilogue_kernel(GemmArgs args, int splits, const float* __restrict__ part,
-                       const float* __restrict__ stats) {
+splitk_epilogue_kernel(GemmArgs args, int splits, const float* __restrict__ part) {
     const int M = args.M, N = args.N;
     const int per_row = (EPI == EPI_RESID) ? N : (N >> 1);
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long)M * per_row) return;
     const int m = (int)(idx / per_row);
     const int c = (int)(idx - (long)m * per_row);
-    float sc = 1.0f;
-    if constexpr (NORM) {
-        float s = 0.f;
-        for (int sp = 0; sp < splits; ++sp) s += stats[(size_t)sp * M + m];
-        sc = inv_rms(s, args.K, args.eps);
-    }
+    const float sc = (EPI == EPI_RESID) ? 1.0f : row_scale(args, m);
     auto sum_col = [&](int n) {
         float v = 0.f;
         for (int sp = 0; sp < splits; ++sp) v += part[((size_t)sp * M + m) * N + n];
@@ -174,21 +162,42 @@ splitk_epilogue_kernel(GemmArgs args, int splits, const float* __restrict__ part
     }
 }
 
-template <int MT, bool NORM>
-hipError_t launch_main(const GemmArgs& a, int splits, float* part, float* stats, hipStream_t s) {
+// EPI_RESID_NORM for decode: one workgroup per row; h = resid + sum of the
+// partials, the next RMSNorm's operand bf16(h * g) and the full row sum of h^2.
+__global__ void __launch_bounds__(256)
+splitk_resid_norm_kernel(GemmArgs args, int splits, const float* __restrict__ part) {
+    __shared__ float sRed[4];
+    const int M = args.M, N = args.N;
+    const int m = blockIdx.x;
+    const Epilogue& e = args.epi;
+    float ss = 0.f;
+    for (int n = threadIdx.x; n < N; n += 256) {
+        float v = 0.f;
+        for (int sp = 0; sp < splits; ++sp) v += part[((size_t)sp * M + m) * N + n];
+        const float h = epi_resid(e, m, n, N, v);
+        epi_norm_operand(e, m, n, N, h);
+        ss += h * h;
+    }
+    ss = warp_sum(ss);
+    if ((threadIdx.x & 63) == 0) sRed[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) e.ssq_out[m] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+}
+
+template <int MT>
+hipError_t launch_main(const GemmArgs& a, int splits, float* part, hipStream_t s) {
     const int KS = a.K / splits;
-    hipLaunchKernelGGL((gemv_bf16_kernel<MT, NORM>), dim3(a.N / GV_ROWS, splits), dim3(256), 0,
-                       s, a, KS, part, stats);
+    hipLaunchKernelGGL((gemv_bf16_kernel<MT>), dim3(a.N / GV_ROWS, splits), dim3(256), 0, s, a,
+                       KS, part);
     return hipGetLastError();
 }
 
-template <int EPI, bool NORM>
-hipError_t launch_epi(const GemmArgs& a, int splits, const float* part, const float* stats,
-                      hipStream_t s) {
+template <int EPI>
+hipError_t launch_epi(const GemmArgs& a, int splits, const float* part, hipStream_t s) {
     const long per_row = (EPI == EPI_RESID) ? a.N : (a.N >> 1);
     const long total = (long)a.M * per_row;
-    hipLaunchKernelGGL((splitk_epilogue_kernel<EPI, NORM>), dim3((unsigned)((total + 255) / 256)),
-                       dim3(256), 0, s, a, splits, part, stats);
+    hipLaunchKernelGGL((splitk_epilogue_kernel<EPI>), dim3((unsigned)((total + 255) / 256)),
+                       dim3(256), 0, s, a, splits, part);
     return hipGetLastError();
 }
 
@@ -209,32 +218,64 @@ int gemv_bf16_splits(int M, int N, int K) {
 }
 
 size_t gemv_bf16_ws_bytes(int M, int N, int splits) {
-    return (size_t)splits * M * N * sizeof(float) + (size_t)splits * M * sizeof(float);
+    return (size_t)splits * M * N * sizeof(float);
 }
 
 hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_t s) {
     if (a.M <= 0 || a.M > 64 || a.N % GV_ROWS != 0 || splits < 1 ||
         a.K % (splits * GV_KQUANT) != 0)
         return hipErrorInvalidValue;
-    float* part = ws;
-    float* stats = ws + (size_t)splits * a.M * a.N;
-    hipError_t err;
-    const bool norm = a.norm != 0;
-    if (a.M <= 32)
-        err = norm ? launch_main<32, true>(a, splits, part, stats, s)
-                   : launch_main<32, false>(a, splits, part, stats, s);
-    else
-        err = norm ? launch_main<64, true>(a, splits, part, stats, s)
-                   : launch_main<64, false>(a, splits, part, stats, s);
+    hipError_t err = a.M <= 32 ? launch_main<32>(a, splits, ws, s) : launch_main<64>(a, splits, ws, s);
     if (err != hipSuccess) return err;
     switch (a.epi.kind) {
-        case EPI_QKV: return norm ? launch_epi<EPI_QKV, true>(a, splits, part, stats, s)
-                                  : hipErrorInvalidValue;
-        case EPI_SWIGLU: return norm ? launch_epi<EPI_SWIGLU, true>(a, splits, part, stats, s)
-                                     : hipErrorInvalidValue;
-        default: return norm ? hipErrorInvalidValue
-                             : launch_epi<EPI_RESID, false>(a, splits, part, stats, s);
+        case EPI_QKV: return launch_epi<EPI_QKV>(a, splits, ws, s);
+        case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, splits, ws, s);
+        case EPI_RESID: return launch_epi<EPI_RESID>(a, splits, ws, s);
+        case EPI_RESID_NORM:
+            hipLaunchKernelGGL(splitk_resid_norm_kernel, dim3(a.M), dim3(256), 0, s, a, splits, ws);
+            return hipGetLastError();
+        default: return hipErrorInvalidValue;
     }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm operand: one wave per row.  a[m, j] = bf16(x[m, j] * g[j]) (one
+// rounding) and ssq[m] = sum_j x[m, j]^2 accumulated in fp32 across the wave
+// ("Llama 3.1 70B", section "RMSNorm": the reduction is done in fp32).  The
+// inverse RMS itself is applied to the fp32 results of the projection.
+__global__ void __launch_bounds__(256)
+norm_rows_kernel(const float* __restrict__ x, const float* __restrict__ g, bf16_t* __restrict__ a,
+                 float* __restrict__ ssq, int M, int d) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M) return;
+    const float* xr = x + (size_t)row * d;
+    bf16_t* ar = a + (size_t)row * d;
+    float s = 0.f;
+    for (int j = lane * 8; j < d; j += 64 * 8) {
+        const float4 v0 = *(const float4*)(xr + j);
+        const float4 v1 = *(const float4*)(xr + j + 4);
+        const float4 g0 = *(const float4*)(g + j);
+        const float4 g1 = *(const float4*)(g + j + 4);
+        s += v0.x * v0.x + v0.y * v0.y + v0.z * v0.z + v0.w * v0.w;
+        s += v1.x * v1.x + v1.y * v1.y + v1.z * v1.z + v1.w * v1.w;
+        uint4 p;
+        p.x = pack_bf16x2(v0.x * g0.x, v0.y * g0.y);
+        p.y = pack_bf16x2(v0.z * g0.z, v0.w * g0.w);
+        p.z = pack_bf16x2(v1.x * g1.x, v1.y * g1.y);
+        p.w = pack_bf16x2(v1.z * g1.z, v1.w * g1.w);
+        *(uint4*)(ar + j) = p;
+    }
+    s = warp_sum(s);
+    if (lane == 0) ssq[row] = s;
+}
+
+hipError_t norm_rows_launch(const float* x, const float* g, void* a, float* ssq, int M, int d,
+                            hipStream_t s) {
+    if (M <= 0 || d % 8 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(norm_rows_kernel, dim3((M + 3) / 4), dim3(256), 0, s, x, g, (bf16_t*)a, ssq,
+                       M, d);
+    return hipGetLastError();
 }
 
 }  // namespace llb

@@ -7,7 +7,7 @@
 
 namespace llb {
 
-enum EpiKind : int { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum EpiKind : int { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_RESID_NORM = 3 };
 
 // What a projection does with its fp32 result C[m, n] (after the row's inverse
 // RMS is applied when the A operand was normalised).
@@ -24,14 +24,24 @@ struct Epilogue {
     // EPI_RESID: out[m, n] = resid[m, n] + C[m, n]   (fp32, [M, N] row-major)
     const float* resid;
     float* out;
+    // EPI_RESID_NORM: as EPI_RESID, and also the next RMSNorm's operand
+    // a_out[m, n] = bf16(out[m, n] * gain[n]) and the partial sum of out^2 over the
+    // tile's columns, ssq_out[tile_n * M + m] (one partial per column tile).
+    const float* gain;
+    void* a_out;
+    float* ssq_out;
     // EPI_SWIGLU: columns come in 64-wide groups [gate 32 | up 32]; feature
     // f = group*32 + j gets u[m, f] = SiLU(C_gate) * C_up, u is [M, N/2].
     void* u_out;
 };
 
-// C = A . W^T.  A: [M, K] row-major, fp32 when `norm` (then A is scaled by the
-// per-column gain and each row's inverse RMS over its K values) or wdtype;
-// W: [N, K] row-major, wdtype.
+// C = A . W^T.  W: [N, K] row-major, wdtype.
+// bf16 path: A is bf16 [M, K].  For EPI_QKV and EPI_SWIGLU, A holds v * g of an
+// RMSNorm (v the residual stream, g its gain) and the row's inverse RMS
+// 1/sqrt(sum/K + eps), sum = sum_p ssq_in[p*M + m] over ssq_count partials, scales
+// C before the epilogue.
+// fp32 path: A is fp32 [M, K]; when `norm`, the kernel forms the RMSNorm itself
+// (A * gain, row inverse RMS over K).
 struct GemmArgs {
     const void* A;
     const float* gain;
@@ -39,6 +49,8 @@ struct GemmArgs {
     int M, N, K;
     int norm;
     float eps;
+    const float* ssq_in;
+    int ssq_count;
     Epilogue epi;
 };
 
@@ -50,11 +62,15 @@ void gemm_bf16_tile(int tile_cfg, int* bm, int* bn, int* threads);
 int gemm_bf16_num_tile_cfgs();
 
 // Small-M projection (decode, M <= 64): weight-streaming split-K; writes fp32
-// partials [splits][M][N] and per-split row sums of squares [splits][M] to ws,
-// then applies the epilogue in a second pass.
+// partials [splits][M][N] to ws, then a second pass sums them in split order and
+// applies the epilogue (EPI_RESID_NORM: one workgroup per row, full ssq_out[m]).
 size_t gemv_bf16_ws_bytes(int M, int N, int splits);
 int gemv_bf16_splits(int M, int N, int K);
 hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_t s);
+
+// RMSNorm operand: a[m, :] = bf16(x[m, :] * g), ssq[m] = sum_j x[m, j]^2 (fp32).
+hipError_t norm_rows_launch(const float* x, const float* g, void* a, float* ssq, int M, int d,
+                            hipStream_t s);
 
 // ---- fp32 projections (SIMT) ----------------------------------------------
 hipError_t gemm_f32_launch(const GemmArgs& a, hipStream_t s);
