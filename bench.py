@@ -209,6 +209,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--only", default=None, help="time only this workload (diagnostics)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (calibrates the "
+                         "HBM byte counters FETCH_SIZE / WRITE_SIZE against a known size)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the block runs on one "
@@ -218,6 +221,16 @@ def main():
     import torch
     assert torch.cuda.is_available(), "no GPU"
     torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4, "launches": 3}), flush=True)
+        return
 
     name = args.only or HEADLINE
     wl, ms, st = time_workload(name, args.steps, args.warmup)

@@ -91,10 +91,10 @@ attn_prefill_kernel(AttnArgs a) {
     };
 
     // V^T element (dim, key) lives at dim*64 + ((key/4 ^ f(dim)) * 4) + key%4 with
-    // f(dim) = (dim ^ dim/8) & 15: conflict-free both for the transposing stores
-    // (16 lanes, dims 8c+j) and for the fragment reads (16 consecutive dims).
+    // f(dim) = (dim / 2) & 15: the 32 lanes of a fragment read (8 bytes each, 32
+    // consecutive dims, one key granule) then cover all 64 banks.
     auto vt_index = [](int dim, int key) {
-        const int f = (dim ^ (dim >> 3)) & 15;
+        const int f = (dim >> 1) & 15;
         return dim * AP_BKV + ((((key >> 2) ^ f)) << 2) + (key & 3);
     };
 

@@ -207,30 +207,18 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
     return p;
 }
 
-// Picks the prefill tile configuration with the best last-wave utilisation of
-// the 256 compute units; ties go to the larger tile.
+// Picks the prefill tile configuration (see gemm_bf16.hip) from measurements
+// on MI355X: the 256x256 tile (8 waves, 1 workgroup per CU) is the fastest once
+// there are enough row panels to fill the 256 compute units; with fewer, the
+// 256x128 tile with two workgroups per CU wins unless the 256x256 grid still
+// covers most of the GPU.
 int pick_tile(int M, int N) {
-    int best = -1;
-    double best_eff = -1.0;
-    long best_area = 0;
-    for (int cfg = 0; cfg < llb::gemm_bf16_num_tile_cfgs(); ++cfg) {
-        int bm, bn, nt;
-        llb::gemm_bf16_tile(cfg, &bm, &bn, &nt);
-        if (N % bn != 0) continue;
-        const long tiles = (long)((M + bm - 1) / bm) * (N / bn);
-        const int per_cu = (bm * bn >= 256 * 128) ? 1 : 2;
-        const long slots = 256L * per_cu;
-        const long waves = (tiles + slots - 1) / slots;
-        const double eff = (double)tiles / (double)(waves * slots) *
-                           ((double)M / (double)(((M + bm - 1) / bm) * bm));
-        const long area = (long)bm * bn;
-        if (eff > best_eff + 0.02 || (eff > best_eff - 0.02 && area > best_area)) {
-            if (eff > best_eff) best_eff = eff;
-            best = cfg;
-            best_area = area;
-        }
-    }
-    return best;
+    const int pm = (M + 255) / 256;
+    if (N % 256 == 0 && M >= 4096) return 0;
+    if (N % 128 != 0) return -1;
+    if ((long)pm * (N / 128) >= 512) return 1;
+    if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return 0;
+    return M > 128 ? 1 : 2;
 }
 
 // Prefill tile configuration of a bf16 projection (-1 if none fits N).

@@ -7,12 +7,11 @@
 // only synchronisation per k-tile is one `s_waitcnt vmcnt(n)` that retires the
 // oldest stage's copies and one workgroup barrier.
 //
-// LDS rows are BK = 32 bf16 (64 bytes, four 16-byte chunks).  Chunk c of row r
-// is stored at chunk position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the
-// 32 lanes reading one MFMA fragment column (32 consecutive rows, one chunk)
-// spread over all banks for 32- and 64-bank LDS alike.  The DMA writes 1 KB per
-// wave instruction (16 rows); lane i fetches the global chunk that belongs at
-// its fixed LDS slot, which realises the swizzle for free.
+// LDS rows are BK bf16 (BK = 32: 64 bytes, four 16-byte chunks).  Chunk c of
+// row r is stored at chunk position c ^ f(r) (see swz), so the lanes reading
+// one MFMA fragment column (32 consecutive rows, one chunk) hit distinct banks.
+// The DMA writes 1 KB per wave instruction; lane i fetches the global chunk
+// that belongs at its fixed LDS slot, which realises the swizzle for free.
 //
 // Epilogues (see epilogue.cuh) run on the fp32 accumulators:
 //   EPI_QKV        rows scaled by 1/rms(x) from the row-norm kernel's sum of
@@ -29,8 +28,6 @@ namespace llb {
 
 namespace {
 
-constexpr int BK = 32;
-constexpr int STAGES = 4;
 
 // One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's
 // 16 bytes land at LDS byte address lds + 16 * i.  Issued from inline assembly
@@ -48,7 +45,15 @@ LLB_DEV uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
 }
 
-LLB_DEV int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Chunk swizzle of LDS rows (measured conflict-free for ds_read_b128 on gfx950,
+// whose LDS serves 16 lanes x 16 bytes per cycle from 64 four-byte banks):
+// BK = 32 (four 16-byte chunks per 64-byte row): chunk c of row r sits at
+// c ^ ((r >> 2) & 3); BK = 64 (eight chunks per 128-byte row): c ^ ((r >> 1) & 7).
+template <int BK>
+LLB_DEV int swz(int r) {
+    if constexpr (BK == 32) return (r >> 2) & 3;
+    else return (r >> 1) & 7;
+}
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding, expcnt left at its maximum):
 // this wave's copies older than the n most recent have landed in LDS, and its
@@ -67,19 +72,22 @@ LLB_DEV void barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OCC, int EPI>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(OCC)))
 gemm_bf16_kernel(GemmArgs args) {
     constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int CPR_K = BK / 8;              // 16-byte chunks per LDS row
+    constexpr int RPB = 64 / CPR_K;            // rows per 1 KB DMA block
     constexpr int WTM = BM / WAVES_M;
     constexpr int WTN = BN / WAVES_N;
     constexpr int TM = WTM / 32;
     constexpr int TN = WTN / 32;
     constexpr int STAGE_ELEMS = (BM + BN) * BK;
-    constexpr int BLOCKS = (BM + BN) / 16;   // 1 KB DMA blocks per stage
+    constexpr int BLOCKS = (BM + BN) / RPB;  // 1 KB DMA blocks per stage
     constexpr int L = BLOCKS / NW;            // DMA instructions per wave per stage
-    static_assert(BLOCKS % NW == 0 && BM % 16 == 0, "DMA split");
-    static_assert(2 * L < 64, "vmcnt range");
+    static_assert(BLOCKS % NW == 0 && BM % RPB == 0, "DMA split");
+    static_assert((STAGES - 2) * L < 64, "vmcnt range");
+    static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
     static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs in a wave");
 
     __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS];
@@ -89,9 +97,18 @@ gemm_bf16_kernel(GemmArgs args) {
     const int M = args.M, N = args.N, K = args.K;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = N / BN;
+    // Tile order: consecutive ids run on one XCD (xcd_remap); within the id
+    // sequence, groups of up to 8 row panels are walked column by column, so the
+    // ~32 tiles an XCD runs at once form an 8 x 4 block that shares A and W
+    // panels in that XCD's L2.
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-    const int m0 = (tile % tiles_m) * BM;
-    const int tn = tile / tiles_m;
+    constexpr int GM = 8;
+    const int group = tile / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_group = tile - group * (GM * tiles_n);
+    const int m0 = (first_m + in_group % gm) * BM;
+    const int tn = in_group / gm;
     const int n0 = tn * BN;
 
     const int tid = threadIdx.x;
@@ -108,9 +125,9 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int blk = wave + i * NW;
-        const int row = blk * 16 + (lane >> 2);          // row in the [A; W] stage
-        const int chunk = (lane & 3) ^ swz(row);
-        if (blk * 16 < BM) {
+        const int row = blk * RPB + lane / CPR_K;        // row in the [A; W] stage
+        const int chunk = (lane % CPR_K) ^ swz<BK>(row);
+        if (blk * RPB < BM) {
             const int gm = min(m0 + row, M - 1);         // rows past M: any valid row
             src[i] = A + (size_t)gm * K + chunk * 8;
         } else {
@@ -126,7 +143,7 @@ gemm_bf16_kernel(GemmArgs args) {
         for (int i = 0; i < L; ++i) {
             const int blk = wave + i * NW;
             dma16(src[i] + kt * BK,
-                  lds_base + (uint32_t)((st * STAGE_ELEMS + blk * 16 * BK) * sizeof(bf16_t)));
+                  lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
         }
     };
 
@@ -143,10 +160,9 @@ gemm_bf16_kernel(GemmArgs args) {
     }
 
     const int nk = K / BK;
-    static_assert(STAGES == 4, "the main loop below is unrolled over 4 stages");
-    if (0 < nk) issue(0, 0);
-    if (1 < nk) issue(1, 1);
-    if (2 < nk) issue(2, 2);
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < nk) issue(st, st);
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -166,12 +182,12 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int r = wm * WTM + i * 32 + (lane & 31);
-                af[i] = as_bf16x8(*(const uint4*)&a_s[r * BK + ((c ^ swz(r)) << 3)]);
+                af[i] = as_bf16x8(*(const uint4*)&a_s[r * BK + ((c ^ swz<BK>(r)) << 3)]);
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int r = wn * WTN + j * 32 + (lane & 31);
-                bfr[j] = as_bf16x8(*(const uint4*)&b_s[r * BK + ((c ^ swz(r)) << 3)]);
+                bfr[j] = as_bf16x8(*(const uint4*)&b_s[r * BK + ((c ^ swz<BK>(r)) << 3)]);
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -179,89 +195,95 @@ gemm_bf16_kernel(GemmArgs args) {
                 for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
     };
-    // One k-tile: retire its copies (later ones stay in flight), barrier, refill
-    // the stage that was read one step earlier, multiply.
+    // One k-tile: retire its copies (the STAGES-2 later ones stay in flight),
+    // barrier, refill the stage that was read one step earlier, multiply.
     auto step = [&](int kt, int rd, int wr) {
-        if (kt + 2 < nk) wait_vm_lgkm<2 * L>();
-        else if (kt + 1 < nk) wait_vm_lgkm<L>();
+        const int later = min(STAGES - 2, nk - 1 - kt);
+        if (STAGES >= 4 && later >= 2) wait_vm_lgkm<(STAGES >= 4 ? 2 : 0) * L>();
+        else if (STAGES >= 3 && later >= 1) wait_vm_lgkm<(STAGES >= 3 ? 1 : 0) * L>();
         else wait_vm_lgkm<0>();
         barrier();
         if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, wr);
         compute(rd);
     };
-    for (int kt = 0; kt < nk; kt += 4) {
-        step(kt, 0, 3);
-        if (kt + 1 < nk) step(kt + 1, 1, 0);
-        if (kt + 2 < nk) step(kt + 2, 2, 1);
-        if (kt + 3 < nk) step(kt + 3, 3, 2);
+    // unrolled over the stages so that every stage offset is a constant
+    for (int kt = 0; kt < nk; kt += STAGES) {
+#pragma unroll
+        for (int st = 0; st < STAGES; ++st)
+            if (kt + st < nk) step(kt + st, st, (st + STAGES - 1) % STAGES);
     }
     __syncthreads();  // no copies are in flight here; orders the sScale writes too
 
-    // ---- epilogue: each 32-row slice of a wave's tile goes through LDS so that a
-    // lane owns 8 consecutive columns of a row (RoPE pairs and gate/up pairs in
-    // one thread, 16-byte stores).
+    // ---- epilogue: each 16-row half of a 32-row slice of a wave's tile goes
+    // through LDS so that a lane owns 8 consecutive columns of a row (RoPE pairs
+    // and gate/up pairs in one thread, 16-byte stores).
     const Epilogue& e = args.epi;
+    constexpr int HR = 16;                        // rows staged at a time per wave
     constexpr int SROW = WTN + 4;                 // padded fp32 row of the staging slice
-    static_assert(4 * 32 * SROW * 4 <= STAGES * STAGE_ELEMS * 2, "staging fits in the stages");
-    float* stile = (float*)smem + wave * (32 * SROW);
+    static_assert(NW * HR * SROW * 4 <= STAGES * STAGE_ELEMS * 2, "staging fits in the stages");
+    float* stile = (float*)smem + wave * (HR * SROW);
     constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int rbase = wm * WTM + i * 32;      // tile row of the slice's first row
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const float sc = SCALED ? sScale[rbase + rr] : 1.0f;
+        for (int half = 0; half < 2; ++half) {
+            const int rbase = wm * WTM + i * 32 + half * HR;   // tile row of the staged rows
 #pragma unroll
-            for (int j = 0; j < TN; ++j) stile[rr * SROW + j * 32 + (lane & 31)] = acc[i][j][r] * sc;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if constexpr (EPI == EPI_SWIGLU) {
-            constexpr int CPR = WTN / 16;         // (gate, up) chunk pairs per row
-            for (int idx = lane; idx < 32 * CPR; idx += 64) {
-                const int row = idx / CPR, ch = idx % CPR;
-                const int cg = (ch >> 2) * 64 + (ch & 3) * 8;   // gate columns in the slice
-                const int m = m0 + rbase + row;
-                float g[8], u[8];
-                *(float4*)&g[0] = *(const float4*)&stile[row * SROW + cg];
-                *(float4*)&g[4] = *(const float4*)&stile[row * SROW + cg + 4];
-                *(float4*)&u[0] = *(const float4*)&stile[row * SROW + cg + 32];
-                *(float4*)&u[4] = *(const float4*)&stile[row * SROW + cg + 36];
-                const int f = ((n0 + wn * WTN + cg - (cg & 63)) >> 1) + (cg & 63);
-                if (m < M) epi_swiglu8(e, m, f, N >> 1, g, u);
+            for (int r = 8 * half; r < 8 * half + 8; ++r) {
+                const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - half * HR;
+                const float sc = SCALED ? sScale[rbase + rr] : 1.0f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    stile[rr * SROW + j * 32 + (lane & 31)] = acc[i][j][r] * sc;
             }
-        } else {
-            constexpr int CPR = WTN / 8;          // 8-column chunks per row
-            for (int idx = lane; idx < 32 * CPR; idx += 64) {
-                const int row = idx / CPR, ch = idx % CPR;
-                const int m = m0 + rbase + row;
-                const int n = n0 + wn * WTN + ch * 8;
-                float v[8];
-                *(float4*)&v[0] = *(const float4*)&stile[row * SROW + ch * 8];
-                *(float4*)&v[4] = *(const float4*)&stile[row * SROW + ch * 8 + 4];
-                if constexpr (EPI == EPI_QKV) {
-                    if (m < M) epi_qkv8(e, m, n, v);
-                } else {
-                    float ss = 0.f;
-                    if (m < M) {
-                        epi_resid8(e, m, n, N, v);
-                        if constexpr (EPI == EPI_RESID_NORM) ss = epi_norm_operand8(e, m, n, N, v);
-                    }
-                    if constexpr (EPI == EPI_RESID_NORM) {
-                        // the CPR lanes of one row are consecutive: reduce over them
-                        static_assert(CPR == 16 || CPR == 8, "row reduction width");
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if constexpr (EPI == EPI_SWIGLU) {
+                constexpr int CPR = WTN / 16;         // (gate, up) chunk pairs per row
+                for (int idx = lane; idx < HR * CPR; idx += 64) {
+                    const int row = idx / CPR, ch = idx % CPR;
+                    const int cg = (ch >> 2) * 64 + (ch & 3) * 8;   // gate columns in the slice
+                    const int m = m0 + rbase + row;
+                    float g[8], u[8];
+                    *(float4*)&g[0] = *(const float4*)&stile[row * SROW + cg];
+                    *(float4*)&g[4] = *(const float4*)&stile[row * SROW + cg + 4];
+                    *(float4*)&u[0] = *(const float4*)&stile[row * SROW + cg + 32];
+                    *(float4*)&u[4] = *(const float4*)&stile[row * SROW + cg + 36];
+                    const int f = ((n0 + wn * WTN + cg - (cg & 63)) >> 1) + (cg & 63);
+                    if (m < M) epi_swiglu8(e, m, f, N >> 1, g, u);
+                }
+            } else {
+                constexpr int CPR = WTN / 8;          // 8-column chunks per row
+                for (int idx = lane; idx < HR * CPR; idx += 64) {
+                    const int row = idx / CPR, ch = idx % CPR;
+                    const int m = m0 + rbase + row;
+                    const int n = n0 + wn * WTN + ch * 8;
+                    float v[8];
+                    *(float4*)&v[0] = *(const float4*)&stile[row * SROW + ch * 8];
+                    *(float4*)&v[4] = *(const float4*)&stile[row * SROW + ch * 8 + 4];
+                    if constexpr (EPI == EPI_QKV) {
+                        if (m < M) epi_qkv8(e, m, n, v);
+                    } else {
+                        float ss = 0.f;
+                        if (m < M) {
+                            epi_resid8(e, m, n, N, v);
+                            if constexpr (EPI == EPI_RESID_NORM) ss = epi_norm_operand8(e, m, n, N, v);
+                        }
+                        if constexpr (EPI == EPI_RESID_NORM) {
+                            // the CPR lanes of one row are consecutive: reduce over them
+                            static_assert(CPR == 16 || CPR == 8, "row reduction width");
 #pragma unroll
-                        for (int off = 1; off < CPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
-                        if ((lane % CPR) == 0) sPart[wn * BM + rbase + row] = ss;
+                            for (int off = 1; off < CPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                            if ((lane % CPR) == 0) sPart[wn * BM + rbase + row] = ss;
+                        }
                     }
                 }
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     if constexpr (EPI == EPI_RESID_NORM) {
@@ -279,30 +301,37 @@ gemm_bf16_kernel(GemmArgs args) {
 }
 
 struct TileCfg {
-    int bm, bn, wm, wn;
+    int bm, bn, wm, wn, bk, stages, occ;
 };
+// The first three are the configurations the host chooses between; the rest
+// are kept for tuning experiments.
 constexpr TileCfg kTiles[] = {
-    {256, 256, 2, 2},  // 4 waves, wave tile 128x128
-    {256, 128, 2, 2},  // 4 waves, wave tile 128x64
-    {128, 128, 2, 2},  // 4 waves, wave tile 64x64
+    {256, 256, 4, 2, 64, 2, 2},  // 8 waves (2 per SIMD), wave tile 64x128, BK 64, 128 KB LDS
+    {256, 128, 2, 2, 32, 3, 2},  // 4 waves, wave tile 128x64, 72 KB: 2 workgroups per CU
+    {128, 128, 2, 2, 32, 4, 2},  // 4 waves, wave tile 64x64, 64 KB: 2 workgroups per CU
+    {256, 256, 2, 4, 32, 4, 2},  // 8 waves, wave tile 128x64
+    {256, 128, 2, 2, 64, 3, 1},  // BK 64, 3 stages (144 KB)
+    {256, 256, 2, 2, 32, 4, 1},  // 4 waves (1 per SIMD), wave tile 128x128
+    {256, 128, 2, 2, 32, 4, 1},  // 4 waves, 4 stages (96 KB)
+    {256, 256, 4, 2, 32, 4, 2},  // 8 waves, BK 32, 4 stages (128 KB)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int ST, int OCC, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(tiles), dim3(64 * WM * WN),
-                       0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, ST, OCC, EPI>), dim3(tiles),
+                       dim3(64 * WM * WN), 0, s, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int ST, int OCC>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     switch (a.epi.kind) {
-        case EPI_QKV: return launch_one<BM, BN, WM, WN, EPI_QKV>(a, s);
-        case EPI_SWIGLU: return launch_one<BM, BN, WM, WN, EPI_SWIGLU>(a, s);
-        case EPI_RESID: return launch_one<BM, BN, WM, WN, EPI_RESID>(a, s);
-        case EPI_RESID_NORM: return launch_one<BM, BN, WM, WN, EPI_RESID_NORM>(a, s);
+        case EPI_QKV: return launch_one<BM, BN, WM, WN, BK, ST, OCC, EPI_QKV>(a, s);
+        case EPI_SWIGLU: return launch_one<BM, BN, WM, WN, BK, ST, OCC, EPI_SWIGLU>(a, s);
+        case EPI_RESID: return launch_one<BM, BN, WM, WN, BK, ST, OCC, EPI_RESID>(a, s);
+        case EPI_RESID_NORM: return launch_one<BM, BN, WM, WN, BK, ST, OCC, EPI_RESID_NORM>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -320,11 +349,16 @@ void gemm_bf16_tile(int cfg, int* bm, int* bn, int* threads) {
 hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
     if (cfg < 0 || cfg >= kNumTiles) return hipErrorInvalidValue;
     const TileCfg t = kTiles[cfg];
-    if (a.M <= 0 || a.N % t.bn != 0 || a.K % BK != 0 || a.K / BK < 1) return hipErrorInvalidValue;
+    if (a.M <= 0 || a.N % t.bn != 0 || a.K % t.bk != 0 || a.K / t.bk < 1) return hipErrorInvalidValue;
     switch (cfg) {
-        case 0: return launch_cfg<256, 256, 2, 2>(a, s);
-        case 1: return launch_cfg<256, 128, 2, 2>(a, s);
-        default: return launch_cfg<128, 128, 2, 2>(a, s);
+        case 0: return launch_cfg<256, 256, 4, 2, 64, 2, 2>(a, s);
+        case 1: return launch_cfg<256, 128, 2, 2, 32, 3, 2>(a, s);
+        case 2: return launch_cfg<128, 128, 2, 2, 32, 4, 2>(a, s);
+        case 3: return launch_cfg<256, 256, 2, 4, 32, 4, 2>(a, s);
+        case 4: return launch_cfg<256, 128, 2, 2, 64, 3, 1>(a, s);
+        case 5: return launch_cfg<256, 256, 2, 2, 32, 4, 1>(a, s);
+        case 6: return launch_cfg<256, 128, 2, 2, 32, 4, 1>(a, s);
+        default: return launch_cfg<256, 256, 4, 2, 32, 4, 2>(a, s);
     }
 }
 

@@ -83,6 +83,7 @@ BF16_SMALL = [
     (512, 4, 4, 512, 1, 33, False),      # MHA
     (768, 4, 2, 1280, 3, 64, False),     # group of 2, d not a multiple of 512
     (512, 8, 2, 768, 1, 300, False),     # several query/key tiles, many row tiles
+    (512, 8, 2, 768, 2, 2100, False),    # M = 4200: the 256x256 projection tiles, ragged M
 ]
 
 
