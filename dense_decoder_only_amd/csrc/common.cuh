@@ -14,15 +14,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 LLB_DEV float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite).
-LLB_DEV bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+LLB_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 LLB_DEV uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // 8 fp32 -> one MFMA bf16x8 operand (element 0 in the low half of word 0).
@@ -84,4 +83,44 @@ LLB_DEV int xcd_remap(int bid, int nblocks) {
     constexpr int XCD = 8;
     if (nblocks % XCD != 0) return bid;
     return (bid % XCD) * (nblocks / XCD) + bid / XCD;
+}
+
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's
+// 16 bytes land at LDS byte address lds + 16 * i.  Issued from inline assembly
+// so that the compiler does not treat every later LDS read as depending on it
+// (it would otherwise wait for all copies in flight before each read); the
+// kernel retires the copies itself with s_waitcnt vmcnt.
+LLB_DEV void dma16(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
+LLB_DEV uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding, expcnt left at its maximum):
+// this wave's copies older than the n most recent have landed in LDS, and its
+// own LDS reads have completed.
+template <int N>
+LLB_DEV void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70);
+}
+
+// s_waitcnt vmcnt(n) alone (lgkmcnt and expcnt left at their maxima).
+template <int N>
+LLB_DEV void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding DMA copy); the empty asm keeps the compiler from
+// moving LDS accesses across it.
+LLB_DEV void barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }

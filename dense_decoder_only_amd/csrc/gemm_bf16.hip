@@ -29,22 +29,6 @@ namespace llb {
 namespace {
 
 
-// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's
-// 16 bytes land at LDS byte address lds + 16 * i.  Issued from inline assembly
-// so that the compiler does not treat every later LDS read as depending on it
-// (it would otherwise wait for all copies in flight before each read); the
-// kernel retires the copies itself with s_waitcnt vmcnt.
-LLB_DEV void dma16(const void* gptr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(lds)
-                 : "memory", "m0");
-}
-
-LLB_DEV uint32_t lds_offset(const void* p) {
-    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-}
-
 // Chunk swizzle of LDS rows (measured conflict-free for ds_read_b128 on gfx950,
 // whose LDS serves 16 lanes x 16 bytes per cycle from 64 four-byte banks):
 // BK = 32 (four 16-byte chunks per 64-byte row): chunk c of row r sits at
@@ -53,23 +37,6 @@ template <int BK>
 LLB_DEV int swz(int r) {
     if constexpr (BK == 32) return (r >> 2) & 3;
     else return (r >> 1) & 7;
-}
-
-// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding, expcnt left at its maximum):
-// this wave's copies older than the n most recent have landed in LDS, and its
-// own LDS reads have completed.
-template <int N>
-LLB_DEV void wait_vm_lgkm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70);
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which would
-// wait for every outstanding DMA copy); the empty asm keeps the compiler from
-// moving LDS accesses across it.
-LLB_DEV void barrier() {
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OCC, int EPI>

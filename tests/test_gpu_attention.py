@@ -54,6 +54,7 @@ def _oracle_prefill(q, kc, vc, pos0, T):
     (4, 1, 1, 0), (4, 2, 31, 0), (4, 1, 64, 0), (4, 2, 100, 0), (4, 1, 300, 0),
     (8, 1, 130, 0), (1, 2, 70, 0), (2, 1, 65, 0),
     (4, 2, 50, 17), (8, 1, 33, 64), (4, 1, 1, 500),
+    (4, 1, 1000, 0), (8, 1, 513, 37), (4, 2, 257, 300), (2, 1, 400, 5), (1, 1, 200, 3),
 ])
 def test_attention_prefill_random(G, B, T, pos0):
     shp, blk, _ = _block(G)
@@ -104,6 +105,34 @@ def test_attention_prefill_structured_mask(shift, pos0, T):
         ref = _oracle_prefill(q, kc, vc, pos0, T)
         e = bf16_err(o.cpu(), ref, c=1e-3)
         note(f"  bf16 err {e:.3f}")
+        assert e <= 1.0
+    finally:
+        llb.llb_block_destroy(blk)
+
+
+def test_attention_prefill_growing_scores():
+    """Scores rise along the keys (score of key n for the query at p is
+    0.05 n + noise), so the softmax offset keeps moving up tile after tile:
+    a running maximum that is not raised far enough, or a rescale that is
+    applied to the wrong rows, shows as a relative error far above bf16."""
+    shp, blk, _ = _block(4)
+    try:
+        B, H, Hkv, hd = 1, shp.n_heads, 2, 128
+        T, pos0 = 900, 0
+        cap = workloads.cache_capacity(pos0 + T)
+        gen = torch.Generator().manual_seed(91)
+        kc = _rand((B, Hkv, cap, hd), gen, 0.05)
+        kc[:, :, :, 0] = (torch.arange(cap, dtype=torch.float32) * 0.05 / 4.0).to(torch.bfloat16)
+        vc = _rand((B, Hkv, cap, hd), gen)
+        q = _rand((B, H, T, hd), gen, 0.05)
+        q[..., 0] = 4.0 * math.sqrt(hd)
+        note("attn prefill growing scores")
+        o = torch.empty(B, T, H * hd, dtype=torch.bfloat16, device="cuda")
+        llb.llb_attention_prefill(blk, q.cuda(), kc.cuda(), vc.cuda(), o, B, T, pos0, cap)
+        ref = _oracle_prefill(q, kc, vc, pos0, T)
+        mag = _oracle_prefill(q, kc, vc.abs(), pos0, T)
+        e = bf16_err(o.cpu(), ref, c=1e-3, mag=mag)
+        note(f"  bf16 err {e:.3f} (max/rms {rel_err(o.cpu(), ref):.2e})")
         assert e <= 1.0
     finally:
         llb.llb_block_destroy(blk)
