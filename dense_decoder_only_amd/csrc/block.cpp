@@ -207,24 +207,30 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
     return p;
 }
 
-// Picks the prefill tile configuration (see gemm_bf16.hip) from measurements
-// on MI355X: the 256x256 tile (8 waves, 1 workgroup per CU) is the fastest once
-// there are enough row panels to fill the 256 compute units; with fewer, the
-// 256x128 tile with two workgroups per CU wins unless the 256x256 grid still
-// covers most of the GPU.
-int pick_tile(int M, int N) {
+// Picks the prefill tile configuration (see gemm_bf16.hip) of C[M,N] = A[M,K] W^T
+// from measurements of the whole block on MI355X:
+//  - long inputs (M >= 4096): 256x256 tiles; the interleaved 4-wave kernel for
+//    the long-K or wide projections, the 8-wave kernel otherwise;
+//  - 256x256 tiles filling at least 2 rounds of the 256 compute units: the
+//    interleaved kernel; at least 160 tiles: the 8-wave kernel;
+//  - otherwise 256x128 tiles: BK 64 with one workgroup per CU when there is
+//    about one tile per CU, BK 32 with two workgroups per CU beyond that.
+int pick_tile(int M, int N, int K) {
     const int pm = (M + 255) / 256;
-    if (N % 256 == 0 && M >= 4096) return 0;
+    if (N % 256 == 0 && M >= 4096) return (K >= 16384 || N >= 32768) ? 3 : 0;
     if (N % 128 != 0) return -1;
-    if ((long)pm * (N / 128) >= 512) return 1;
+    if (N % 256 == 0 && (long)pm * (N / 256) >= 512) return 3;
     if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return 0;
+    const long t128 = (long)pm * (N / 128);
+    if (t128 >= 512) return 1;
+    if (t128 >= 192 && K % 64 == 0) return 5;
     return M > 128 ? 1 : 2;
 }
 
 // Prefill tile configuration of a bf16 projection (-1 if none fits N).
-int tile_for(const llb_block* b, int override_cfg, int M, int N) {
+int tile_for(const llb_block* b, int override_cfg, int M, int N, int K) {
     (void)b;
-    return override_cfg >= 0 ? override_cfg : pick_tile(M, N);
+    return override_cfg >= 0 ? override_cfg : pick_tile(M, N, K);
 }
 
 llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, float* scratch,
@@ -287,7 +293,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = x; a.gain = b->g1; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_QKV; a.epi.q_out = q; a.epi.k_cache = kc; a.epi.v_cache = vc;
-    llb_status st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_qkv, M, nqkv), s,
+    llb_status st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_qkv, M, nqkv, d), s,
                              "qkv projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
@@ -304,7 +310,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
     // 3. h = x + O . Wo^T   (bf16: also the FFN RMSNorm's operand and row sums of h^2)
-    const int tile_o = tile_for(b, b->tile_o, M, d);
+    const int tile_o = tile_for(b, b->tile_o, M, d, c.n_heads * c.head_dim);
     a = llb::GemmArgs{};
     a.A = o; a.W = b->wo; a.M = M; a.N = d; a.K = c.n_heads * hd; a.eps = c.eps;
     a.epi = e; a.epi.resid = x; a.epi.out = h;
@@ -333,7 +339,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = h; a.gain = b->g2; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
-    st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_gu, M, 2 * c.d_ff), s,
+    st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_gu, M, 2 * c.d_ff, d), s,
                   "gate/up projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
@@ -342,7 +348,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     a = llb::GemmArgs{};
     a.A = u; a.W = b->wdown; a.M = M; a.N = d; a.K = c.d_ff; a.eps = c.eps;
     a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = h; a.epi.out = y;
-    st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_down, M, d), s, "down projection");
+    st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_down, M, d, c.d_ff), s, "down projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
     return LLB_OK;

@@ -20,6 +20,8 @@
 //   EPI_RESID_NORM out = h = resid + C, plus the operand of the next RMSNorm,
 //                  bf16(h * g), and this tile's partial sum of h^2 per row;
 //   EPI_SWIGLU     rows scaled by 1/rms(h) from those partials, SiLU(gate)*up.
+#include <type_traits>
+
 #include "common.cuh"
 #include "epilogue.cuh"
 #include "kernels.h"
@@ -39,7 +41,9 @@ LLB_DEV int swz(int r) {
     else return (r >> 1) & 7;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OCC, int EPI>
+constexpr int SCHED_PLAIN = 0, SCHED_INTERLEAVE = 1;
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OCC, int EPI, int SCHED>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(OCC)))
 gemm_bf16_kernel(GemmArgs args) {
     constexpr int NW = WAVES_M * WAVES_N;
@@ -54,12 +58,10 @@ gemm_bf16_kernel(GemmArgs args) {
     constexpr int L = BLOCKS / NW;            // DMA instructions per wave per stage
     static_assert(BLOCKS % NW == 0 && BM % RPB == 0, "DMA split");
     static_assert((STAGES - 2) * L < 64, "vmcnt range");
-    static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+    static_assert(STAGES >= 2 && STAGES <= (SCHED == SCHED_INTERLEAVE ? 5 : 4), "pipeline depth");
     static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs in a wave");
 
     __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS];
-    __shared__ float sScale[BM];
-    __shared__ float sPart[(EPI == EPI_RESID_NORM) ? WAVES_N * BM : 1];
 
     const int M = args.M, N = args.N, K = args.K;
     const int tiles_m = (M + BM - 1) / BM;
@@ -81,6 +83,14 @@ gemm_bf16_kernel(GemmArgs args) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Main-loop schedules: SCHED_PLAIN (per k-tile: wait, barrier, copies,
+    // fragment reads and MFMAs, with latency hidden by the other waves of the
+    // SIMD) and SCHED_INTERLEAVE (one wave per SIMD, its LDS reads and copies
+    // threaded between its MFMAs).
+    static_assert(SCHED != SCHED_INTERLEAVE ||
+                      (NW == 4 && TM == 4 && TN == 4 && (BK == 32 || BK == 64) && STAGES >= 2 &&
+                       L <= 8 * (BK / 16 - 1)),
+                  "interleaved shape");
     const int wm = wave % WAVES_M;
     const int wn = wave / WAVES_M;
 
@@ -114,15 +124,19 @@ gemm_bf16_kernel(GemmArgs args) {
         }
     };
 
-    // row scales for the normalised-operand epilogues (before the first copies
-    // are issued, so that waiting for these loads does not drain the pipeline)
-    if constexpr (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
-        for (int i = tid; i < BM; i += 64 * NW) {
-            const int m = m0 + i;
+    // Row scale of the normalised-operand epilogues, loaded before the first
+    // copies are issued (waiting for these loads does not drain the pipeline)
+    // and parked in LDS after the main loop.  Every row of the tile has one
+    // thread (BM <= threads).
+    static_assert(BM <= 64 * NW, "one thread per tile row");
+    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+    float row_scale = 1.0f;
+    if constexpr (SCALED) {
+        const int m = m0 + tid;
+        if (tid < BM && m < M) {
             float s = 0.f;
-            if (m < M)
-                for (int p = 0; p < args.ssq_count; ++p) s += args.ssq_in[(size_t)p * M + m];
-            sScale[i] = inv_rms(s, K, args.eps);
+            for (int p = 0; p < args.ssq_count; ++p) s += args.ssq_in[(size_t)p * M + m];
+            row_scale = inv_rms(s, K, args.eps);
         }
     }
 
@@ -162,34 +176,134 @@ gemm_bf16_kernel(GemmArgs args) {
                 for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
     };
-    // One k-tile: retire its copies (the STAGES-2 later ones stay in flight),
-    // barrier, refill the stage that was read one step earlier, multiply.
-    auto step = [&](int kt, int rd, int wr) {
-        const int later = min(STAGES - 2, nk - 1 - kt);
-        if (STAGES >= 4 && later >= 2) wait_vm_lgkm<(STAGES >= 4 ? 2 : 0) * L>();
-        else if (STAGES >= 3 && later >= 1) wait_vm_lgkm<(STAGES >= 3 ? 1 : 0) * L>();
-        else wait_vm_lgkm<0>();
-        barrier();
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, wr);
-        compute(rd);
-    };
-    // unrolled over the stages so that every stage offset is a constant
-    for (int kt = 0; kt < nk; kt += STAGES) {
+    if constexpr (SCHED == SCHED_PLAIN) {
+        // One k-tile: retire its copies (the STAGES-2 later ones stay in flight),
+        // barrier, refill the stage that was read one step earlier, multiply.
+        auto step = [&](int kt, int rd, int wr) {
+            const int later = min(STAGES - 2, nk - 1 - kt);
+            if (STAGES >= 4 && later >= 2) wait_vm_lgkm<(STAGES >= 4 ? 2 : 0) * L>();
+            else if (STAGES >= 3 && later >= 1) wait_vm_lgkm<(STAGES >= 3 ? 1 : 0) * L>();
+            else wait_vm_lgkm<0>();
+            barrier();
+            if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, wr);
+            compute(rd);
+        };
+        // unrolled over the stages so that every stage offset is a constant
+        for (int kt = 0; kt < nk; kt += STAGES) {
+    #pragma unroll
+            for (int st = 0; st < STAGES; ++st)
+                if (kt + st < nk) step(kt + st, st, (st + STAGES - 1) % STAGES);
+        }
+    } else {
+        // Interleaved: one wave per SIMD owns a 128x128 block.  Within k-tile t
+        // (two k-steps of 16), the 16 MFMAs of step 0 are threaded with the
+        // LDS reads of step 1's fragments and the copies of k-tile t+STAGES-1
+        // into the stage of k-tile t-1; the 16 MFMAs of step 1 are split around the
+        // wait + barrier that publishes k-tile t+1, after which step 0's
+        // fragments of k-tile t+1 are read between the last 8 MFMAs.  Every
+        // element is pinned in place with a scheduling barrier.
+        bf16x8 fa[2][TM], fb[2][TN];
+        constexpr int KS = BK / 16;
+        uint32_t a_off[KS], b_off[KS];
 #pragma unroll
-        for (int st = 0; st < STAGES; ++st)
-            if (kt + st < nk) step(kt + st, st, (st + STAGES - 1) % STAGES);
+        for (int kk = 0; kk < KS; ++kk) {
+            const int c = 2 * kk + (lane >> 5);
+            const int ra = wm * WTM + (lane & 31), rb = wn * WTN + (lane & 31);
+            a_off[kk] = lds_base + (uint32_t)((ra * BK + ((c ^ swz<BK>(ra)) << 3)) * 2);
+            b_off[kk] = lds_base + (uint32_t)((BM * BK + rb * BK + ((c ^ swz<BK>(rb)) << 3)) * 2);
+        }
+        constexpr uint32_t STAGE_BYTES = STAGE_ELEMS * 2;
+        typedef bf16x8 __attribute__((address_space(3))) * lds_frag_ptr;
+        auto rd_a = [&](int st, int kk, int fbuf, int i) {
+            fa[fbuf][i] = *(lds_frag_ptr)(uintptr_t)(a_off[kk] + st * STAGE_BYTES + i * 32 * BK * 2);
+        };
+        auto rd_b = [&](int st, int kk, int fbuf, int j) {
+            fb[fbuf][j] = *(lds_frag_ptr)(uintptr_t)(b_off[kk] + st * STAGE_BYTES + j * 32 * BK * 2);
+        };
+        // n-th of the 8 fragment reads, in the order the MFMAs (i-major) first
+        // use them: A0 B0 B1 B2 B3 A1 A2 A3
+        auto rd = [&](int st, int kk, int fbuf, int n) {
+            if (n == 0) rd_a(st, kk, fbuf, 0);
+            else if (n <= TN) rd_b(st, kk, fbuf, n - 1);
+            else rd_a(st, kk, fbuf, n - TN);
+        };
+        auto mf = [&](int fbuf, int n) {  // n-th of the 16 MFMAs of a k-step
+            const int i = n / TN, j = n % TN;
+            acc[i][j] = mfma32(fa[fbuf][i], fb[fbuf][j], acc[i][j]);
+        };
+        auto dma_one = [&](int kt, int st, int i) {
+            const int blk = wave + i * NW;
+            dma16(src[i] + kt * BK, lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
+        };
+        // the prologue issued k-tiles 0..STAGES-2 (clamped copies for small K
+        // keep the count): k-tile 0 landed once (STAGES-2) L copies are pending
+        for (int t = nk; t < STAGES - 1; ++t)
+            for (int i = 0; i < L; ++i) dma_one(nk - 1, t, i);
+        wait_vm_lgkm<(STAGES - 2) * L>();
+        barrier();
+#pragma unroll
+        for (int n = 0; n < 8; ++n) rd(0, 0, 0, n);
+        // The body is the same for every k-tile: near the end, the copies of
+        // "k-tile t+STAGES-1" repeat the last k-tile into the free stage and
+        // the reads of "k-tile t+1" land in registers that are not used again.
+        auto tile_k = [&](int t, int st) {
+            const int t_copy = min(t + STAGES - 1, nk - 1);
+            const int st_copy = (st + STAGES - 1) % STAGES;
+            const int st_next = (st + 1) % STAGES;
+            // steps 0..KS-2: 16 MFMAs each; the 8 reads of the next step ride
+            // on the first 8, this k-tile's share of the copies on the last 8
+#pragma unroll
+            for (int ks = 0; ks + 1 < KS; ++ks) {
+#pragma unroll
+                for (int n = 0; n < 16; ++n) {
+                    mf(ks & 1, n);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (n < 8) rd(st, ks + 1, (ks + 1) & 1, n);
+                    else if (ks * 8 + n - 8 < L) dma_one(t_copy, st_copy, ks * 8 + n - 8);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            constexpr int LB = (KS - 1) & 1;  // fragment buffer of the last step
+            // last step, first half
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                mf(LB, n);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // k-tile t+1 landed (the copies of the STAGES-2 later ones stay in flight)
+            wait_vm_lgkm<(STAGES - 2) * L>();
+            barrier();
+            // last step, second half, with step 0's fragments of k-tile t+1
+#pragma unroll
+            for (int n = 8; n < 16; ++n) {
+                mf(LB, n);
+                __builtin_amdgcn_sched_barrier(0);
+                rd(st_next, 0, 0, n - 8);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        for (int kt = 0; kt < nk; ++kt) tile_k(kt, kt % STAGES);
+        wait_vm_lgkm<0>();  // the trailing (repeated) copies
     }
-    __syncthreads();  // no copies are in flight here; orders the sScale writes too
+    __syncthreads();  // no copies are in flight here: the stages are free
 
     // ---- epilogue: each 16-row half of a 32-row slice of a wave's tile goes
     // through LDS so that a lane owns 8 consecutive columns of a row (RoPE pairs
-    // and gate/up pairs in one thread, 16-byte stores).
+    // and gate/up pairs in one thread, 16-byte stores).  LDS (reusing the
+    // stages): [staging slices of the NW waves][row scales BM][row partial
+    // sums of squares WAVES_N x BM].
     const Epilogue& e = args.epi;
     constexpr int HR = 16;                        // rows staged at a time per wave
     constexpr int SROW = WTN + 4;                 // padded fp32 row of the staging slice
-    static_assert(NW * HR * SROW * 4 <= STAGES * STAGE_ELEMS * 2, "staging fits in the stages");
+    static_assert((NW * HR * SROW + BM + WAVES_N * BM) * 4 <= STAGES * STAGE_ELEMS * 2,
+                  "epilogue LDS fits in the stages");
     float* stile = (float*)smem + wave * (HR * SROW);
-    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+    float* sScale = (float*)smem + NW * HR * SROW;
+    float* sPart = sScale + BM;
+    if constexpr (SCALED) {
+        if (tid < BM) sScale[tid] = row_scale;
+        __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -268,37 +382,35 @@ gemm_bf16_kernel(GemmArgs args) {
 }
 
 struct TileCfg {
-    int bm, bn, wm, wn, bk, stages, occ;
+    int bm, bn, wm, wn, bk, stages, occ, sched;
 };
 // The first three are the configurations the host chooses between; the rest
 // are kept for tuning experiments.
 constexpr TileCfg kTiles[] = {
-    {256, 256, 4, 2, 64, 2, 2},  // 8 waves (2 per SIMD), wave tile 64x128, BK 64, 128 KB LDS
-    {256, 128, 2, 2, 32, 3, 2},  // 4 waves, wave tile 128x64, 72 KB: 2 workgroups per CU
-    {128, 128, 2, 2, 32, 4, 2},  // 4 waves, wave tile 64x64, 64 KB: 2 workgroups per CU
-    {256, 256, 2, 4, 32, 4, 2},  // 8 waves, wave tile 128x64
-    {256, 128, 2, 2, 64, 3, 1},  // BK 64, 3 stages (144 KB)
-    {256, 256, 2, 2, 32, 4, 1},  // 4 waves (1 per SIMD), wave tile 128x128
-    {256, 128, 2, 2, 32, 4, 1},  // 4 waves, 4 stages (96 KB)
-    {256, 256, 4, 2, 32, 4, 2},  // 8 waves, BK 32, 4 stages (128 KB)
+    {256, 256, 4, 2, 64, 2, 2, 0},  // 8 waves (2 per SIMD), wave tile 64x128, BK 64, 128 KB LDS
+    {256, 128, 2, 2, 32, 3, 2, 0},  // 4 waves, wave tile 128x64, 72 KB: 2 workgroups per CU
+    {128, 128, 2, 2, 32, 4, 2, 0},  // 4 waves, wave tile 64x64, 64 KB: 2 workgroups per CU
+    {256, 256, 2, 2, 64, 2, 1, 1},  // 4 waves (1 per SIMD), wave tile 128x128, interleaved, BK 64
+    {256, 256, 2, 2, 32, 4, 1, 1},  // the same with BK 32 and 4 stages
+    {256, 128, 2, 2, 64, 3, 1, 0},  // 4 waves, BK 64, 3 stages (144 KB)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int BM, int BN, int WM, int WN, int BK, int ST, int OCC, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int ST, int OCC, int SCHED, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
     const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, ST, OCC, EPI>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, ST, OCC, EPI, SCHED>), dim3(tiles),
                        dim3(64 * WM * WN), 0, s, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int ST, int OCC>
+template <int BM, int BN, int WM, int WN, int BK, int ST, int OCC, int SCHED = SCHED_PLAIN>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     switch (a.epi.kind) {
-        case EPI_QKV: return launch_one<BM, BN, WM, WN, BK, ST, OCC, EPI_QKV>(a, s);
-        case EPI_SWIGLU: return launch_one<BM, BN, WM, WN, BK, ST, OCC, EPI_SWIGLU>(a, s);
-        case EPI_RESID: return launch_one<BM, BN, WM, WN, BK, ST, OCC, EPI_RESID>(a, s);
-        case EPI_RESID_NORM: return launch_one<BM, BN, WM, WN, BK, ST, OCC, EPI_RESID_NORM>(a, s);
+        case EPI_QKV: return launch_one<BM, BN, WM, WN, BK, ST, OCC, SCHED, EPI_QKV>(a, s);
+        case EPI_SWIGLU: return launch_one<BM, BN, WM, WN, BK, ST, OCC, SCHED, EPI_SWIGLU>(a, s);
+        case EPI_RESID: return launch_one<BM, BN, WM, WN, BK, ST, OCC, SCHED, EPI_RESID>(a, s);
+        case EPI_RESID_NORM: return launch_one<BM, BN, WM, WN, BK, ST, OCC, SCHED, EPI_RESID_NORM>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -321,11 +433,9 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
         case 0: return launch_cfg<256, 256, 4, 2, 64, 2, 2>(a, s);
         case 1: return launch_cfg<256, 128, 2, 2, 32, 3, 2>(a, s);
         case 2: return launch_cfg<128, 128, 2, 2, 32, 4, 2>(a, s);
-        case 3: return launch_cfg<256, 256, 2, 4, 32, 4, 2>(a, s);
-        case 4: return launch_cfg<256, 128, 2, 2, 64, 3, 1>(a, s);
-        case 5: return launch_cfg<256, 256, 2, 2, 32, 4, 1>(a, s);
-        case 6: return launch_cfg<256, 128, 2, 2, 32, 4, 1>(a, s);
-        default: return launch_cfg<256, 256, 4, 2, 32, 4, 2>(a, s);
+        case 3: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_INTERLEAVE>(a, s);
+        case 4: return launch_cfg<256, 256, 2, 2, 32, 4, 1, SCHED_INTERLEAVE>(a, s);
+        default: return launch_cfg<256, 128, 2, 2, 64, 3, 1>(a, s);
     }
 }
 

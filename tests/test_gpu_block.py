@@ -84,6 +84,8 @@ BF16_SMALL = [
     (768, 4, 2, 1280, 3, 64, False),     # group of 2, d not a multiple of 512
     (512, 8, 2, 768, 1, 300, False),     # several query/key tiles, many row tiles
     (512, 8, 2, 768, 2, 2100, False),    # M = 4200: the 256x256 projection tiles, ragged M
+    (256, 4, 2, 5120, 1, 1000, False),   # gate/up on the interleaved 4-wave kernel, ragged M, K = 256
+    (2048, 16, 4, 512, 1, 3000, False),  # o and down on 256x128 BK-64 tiles, ragged M
 ]
 
 
