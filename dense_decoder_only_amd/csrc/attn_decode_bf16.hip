@@ -93,21 +93,23 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
         for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int kt = k_beg; kt < k_end; kt += 16) {
-        // ---- scores: D[key][head] = K . Q^T
+    // K and V of one 16-key step; the next step's loads are issued before the
+    // current step is computed (two register buffers)
+    auto load_step = [&](int kt, uint4 (&kf)[KST], uint4 (&vf)[KPL]) {
         const int krow = kt + (lane & 15);
-        uint4 kf[KST];
 #pragma unroll
         for (int kk = 0; kk < KST; ++kk)
             kf[kk] = krow < k_end ? *(const uint4*)(Kg + (size_t)krow * HD + 32 * kk + 8 * (lane >> 4))
                                   : make_uint4(0, 0, 0, 0);
-        uint4 vf[KPL];
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
             const int key = kt + ps * KPL + i;
             vf[i] = key < k_end ? *(const uint4*)(Vg + (size_t)key * HD + 8 * pc)
                                 : make_uint4(0, 0, 0, 0);
         }
+    };
+    auto step = [&](int kt, const uint4 (&kf)[KST], const uint4 (&vf)[KPL]) {
+        // ---- scores: D[key][head] = K . Q^T
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KST; ++kk) s = mfma16(as_bf16x8(kf[kk]), qf[kk], s);
@@ -164,6 +166,16 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    uint4 kfa[KST], vfa[KPL], kfb[KST], vfb[KPL];
+    load_step(k_beg, kfa, vfa);
+    for (int kt = k_beg; kt < k_end; kt += 32) {
+        if (kt + 16 < k_end) load_step(kt + 16, kfb, vfb);
+        step(kt, kfa, vfa);
+        if (kt + 16 < k_end) {
+            if (kt + 32 < k_end) load_step(kt + 32, kfa, vfa);
+            step(kt + 16, kfb, vfb);
+        }
     }
 
     // reduce the key slots (lane bits above log2(NC))
@@ -198,8 +210,10 @@ attn_decode_merge_kernel(AttnArgs a, int n_chunks, const float* __restrict__ par
     const int j = threadIdx.x;
     const float* ml = part_ml + (size_t)bh * n_chunks * 2;
     float mmax = -INFINITY;
+#pragma unroll 8
     for (int c = 0; c < n_chunks; ++c) mmax = fmaxf(mmax, ml[2 * c]);
     float den = 0.f, num = 0.f;
+#pragma unroll 8
     for (int c = 0; c < n_chunks; ++c) {
         const float w = exp2f(ml[2 * c] - mmax);
         den += w * ml[2 * c + 1];

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -47,6 +48,8 @@ struct llb_block {
     llb_config cfg;
     int es;          // bytes per weight / cache element
     int device;
+    // Projection weights [N, K] (bf16: in the 128 x 64 tiled layout of
+    // tile_weights_launch; fp32: row-major).
     void* wqkv;      // [(n_heads + 2 n_kv) hd, d]: Q rows, then K, then V
     void* wo;        // [d, n_heads hd]
     void* wgu;       // [2 d_ff, d]: 64-row groups [gate 32 rows | up 32 rows]
@@ -185,7 +188,6 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
         p.ssq1 = off; off += align_up(M * sizeof(float));
         p.ssq2 = off; off += align_up(M * (size_t)(c.d_model / 128) * sizeof(float));
     }
-    p.scratch = off;
     size_t scratch = 0;
     if (decode && c.wdtype == LLB_BF16) {
         const int d = c.d_model, hq = c.n_heads * c.head_dim;
@@ -201,6 +203,7 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
         const size_t att = llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys);
         if (att > scratch) scratch = att;
     }
+    p.scratch = off;
     p.scratch_bytes = scratch;
     off += align_up(scratch);
     p.total = off;
@@ -322,6 +325,8 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
             int bm, bn, nt;
             llb::gemm_bf16_tile(tile_o, &bm, &bn, &nt);
             ssq2_count = d / bn;
+        } else {
+            ssq2_count = llb::gemv_bf16_ssq_parts(d);  // one partial per 128-column tile
         }
     } else {
         a.epi.kind = llb::EPI_RESID;
@@ -412,6 +417,26 @@ llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* s
     if (e == hipSuccess)
         e = hipMemcpy2DAsync((char*)b->wgu + 32 * d * es, 64 * d * es, w->w_up, 32 * d * es,
                              32 * d * es, dff / 32, hipMemcpyDeviceToDevice, s);
+    // bf16 weights go into the projections' 128 x 64 tiled layout (contiguous
+    // 16 KB tiles: whole DRAM pages per pipeline stage)
+    if (e == hipSuccess && c.wdtype == LLB_BF16) {
+        struct { void* p; size_t n, k; } mats[] = {
+            {b->wqkv, nq + 2 * nkv, d}, {b->wo, d, nq}, {b->wgu, 2 * dff, d}, {b->wdown, d, dff}};
+        size_t most = 0;
+        for (auto& m : mats) most = std::max(most, m.n * m.k * es);
+        void* tmp = nullptr;
+        e = hipMalloc(&tmp, most);
+        for (auto& m : mats) {
+            if (e != hipSuccess) break;
+            e = hipMemcpyAsync(tmp, m.p, m.n * m.k * es, hipMemcpyDeviceToDevice, s);
+            if (e == hipSuccess) e = llb::tile_weights_launch(tmp, m.p, (int)m.n, (int)m.k, s);
+        }
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (tmp) {
+            const hipError_t fe = hipFree(tmp);
+            if (e == hipSuccess) e = fe;
+        }
+    }
     // gains: widen to fp32 on the host (bf16 -> fp32 is exact)
     std::vector<unsigned char> graw(d * es);
     std::vector<float> gf(d);

@@ -97,20 +97,32 @@ gemm_bf16_kernel(GemmArgs args) {
     const bf16_t* __restrict__ A = (const bf16_t*)args.A;
     const bf16_t* __restrict__ W = (const bf16_t*)args.W;
 
-    // Per-lane global source of each of this wave's DMA blocks (k0 = 0).
+    // Per-lane global source of each of this wave's DMA blocks (k0 = 0).  A is
+    // row-major [M, K]; W is stored in 128-row x 64-column tiles (see
+    // tile_weights_launch): element (n, k) at
+    // ((n / 128) * (K / 64) + k / 64) * 8192 + (n % 128) * 64 + k % 64.
     const bf16_t* src[L];
+    bool is_w[L];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int blk = wave + i * NW;
         const int row = blk * RPB + lane / CPR_K;        // row in the [A; W] stage
         const int chunk = (lane % CPR_K) ^ swz<BK>(row);
-        if (blk * RPB < BM) {
+        is_w[i] = blk * RPB >= BM;
+        if (!is_w[i]) {
             const int gm = min(m0 + row, M - 1);         // rows past M: any valid row
             src[i] = A + (size_t)gm * K + chunk * 8;
         } else {
-            src[i] = W + (size_t)(n0 + row - BM) * K + chunk * 8;
+            const int wr = n0 + row - BM;
+            src[i] = W + (size_t)(wr >> 7) * (K / 64) * 8192 + (wr & 127) * 64 + chunk * 8;
         }
     }
+    // element offset of k-tile kt from a block's k0 = 0 source
+    auto k_off = [&](int i, int kt) -> size_t {
+        if (!is_w[i]) return (size_t)kt * BK;
+        if constexpr (BK == 64) return (size_t)kt * 8192;
+        else return (size_t)(kt >> 1) * 8192 + (kt & 1) * 32;
+    };
     // Copies of k-tile kt into stage `st` (a compile-time constant at every call:
     // the stage offsets must be constants for the compiler to see that the LDS
     // reads of one stage do not depend on the copies in flight to another).
@@ -119,7 +131,7 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int blk = wave + i * NW;
-            dma16(src[i] + kt * BK,
+            dma16(src[i] + k_off(i, kt),
                   lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
         }
     };
@@ -233,7 +245,7 @@ gemm_bf16_kernel(GemmArgs args) {
         };
         auto dma_one = [&](int kt, int st, int i) {
             const int blk = wave + i * NW;
-            dma16(src[i] + kt * BK, lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
+            dma16(src[i] + k_off(i, kt), lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
         };
         // the prologue issued k-tiles 0..STAGES-2 (clamped copies for small K
         // keep the count): k-tile 0 landed once (STAGES-2) L copies are pending
@@ -381,6 +393,21 @@ gemm_bf16_kernel(GemmArgs args) {
     }
 }
 
+// W [N, K] row-major -> 128 x 64 tiles, tile (N/128, K/64) row-major, each
+// tile row-major (64 elements = 128 bytes per row): a pipeline stage of a
+// projection then reads whole, contiguous 16 KB tiles.  One thread per 8
+// elements.
+__global__ void __launch_bounds__(256)
+tile_weights_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int N, int K) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;  // 8-element unit
+    const long units = (long)N * K / 8;
+    if (idx >= units) return;
+    const int n = (int)(idx / (K / 8));
+    const int k = (int)(idx % (K / 8)) * 8;
+    const size_t o = ((size_t)(n >> 7) * (K / 64) + (k >> 6)) * 8192 + (n & 127) * 64 + (k & 63);
+    *(uint4*)(dst + o) = *(const uint4*)(src + (size_t)n * K + k);
+}
+
 struct TileCfg {
     int bm, bn, wm, wn, bk, stages, occ, sched;
 };
@@ -418,6 +445,14 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 int gemm_bf16_num_tile_cfgs() { return kNumTiles; }
+
+hipError_t tile_weights_launch(const void* src, void* dst, int N, int K, hipStream_t s) {
+    if (N <= 0 || K <= 0 || N % 128 != 0 || K % 64 != 0 || src == dst) return hipErrorInvalidValue;
+    const long units = (long)N * K / 8;
+    hipLaunchKernelGGL(tile_weights_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s,
+                       (const bf16_t*)src, (bf16_t*)dst, N, K);
+    return hipGetLastError();
+}
 
 void gemm_bf16_tile(int cfg, int* bm, int* bn, int* threads) {
     *bm = kTiles[cfg].bm;

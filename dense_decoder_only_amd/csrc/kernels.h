@@ -35,7 +35,7 @@ struct Epilogue {
     void* u_out;
 };
 
-// C = A . W^T.  W: [N, K] row-major, wdtype.
+// C = A . W^T.  W: [N, K], fp32 row-major or bf16 in the tiled layout below.
 // bf16 path: A is bf16 [M, K].  For EPI_QKV and EPI_SWIGLU, A holds v * g of an
 // RMSNorm (v the residual stream, g its gain) and the row's inverse RMS
 // 1/sqrt(sum/K + eps), sum = sum_p ssq_in[p*M + m] over ssq_count partials, scales
@@ -60,11 +60,18 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int tile_cfg, hipStream_t s);
 // Tile configurations available to gemm_bf16_launch: returns BM, BN, threads.
 void gemm_bf16_tile(int tile_cfg, int* bm, int* bn, int* threads);
 int gemm_bf16_num_tile_cfgs();
+// The bf16 projections read W in 128-row x 64-column tiles: element (n, k) of
+// W [N, K] at ((n/128) * (K/64) + k/64) * 8192 + (n%128) * 64 + k%64.  Converts a
+// row-major W (N % 128 == 0, K % 64 == 0) into that layout (src != dst).
+hipError_t tile_weights_launch(const void* src, void* dst, int N, int K, hipStream_t s);
 
-// Small-M projection (decode, M <= 64): weight-streaming split-K; writes fp32
-// partials [splits][M][N] to ws, then a second pass sums them in split order and
-// applies the epilogue (EPI_RESID_NORM: one workgroup per row, full ssq_out[m]).
+// Small-M projection (decode, M <= 64): weight-streaming split-K over 128-row
+// column tiles.  ws: gemv_bf16_ws_bytes(M, N, splits) bytes of fp32 partials.
+// With several splits a second kernel sums the partials in split order and
+// applies the epilogue.  EPI_RESID_NORM writes one partial sum of squares per
+// column tile, ssq_out[tile * M + m] (gemv_bf16_ssq_parts(N) of them).
 size_t gemv_bf16_ws_bytes(int M, int N, int splits);
+int gemv_bf16_ssq_parts(int N);
 int gemv_bf16_splits(int M, int N, int K);
 hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_t s);
 
