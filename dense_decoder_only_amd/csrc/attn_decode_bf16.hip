@@ -22,6 +22,7 @@ namespace llb {
 namespace {
 
 constexpr int AD_TARGET_WAVES = 4096;
+constexpr int AD_FUSED_MIN_UNITS = 128;  // (sequence, KV head) units for the one-workgroup-per-unit form
 
 struct DecodePlan {
     int n_chunks;
@@ -42,31 +43,21 @@ DecodePlan plan_decode(int B, int n_kv, int n_keys) {
     return p;
 }
 
-template <int HD, int G>
-__global__ void __launch_bounds__(256)
-attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part_o,
-                   float* __restrict__ part_ml) {
+// One wave's share of a decode attention unit (sequence b, KV head g): keys
+// k_beg..k_end-1 for the G query heads of the group, in 16-key steps.  Leaves
+// the unnormalised partial state: m_run, l_run (every lane; base-2 units) and
+// o[h][0..7] = sum_n p_n v_n[8*pc .. 8*pc+8] in lanes pc = lane < HD/8.
+template <int HD, int G, int DEPTH>
+__device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, int k_beg, int k_end,
+                                             float (&sP)[16][16], float (&sAl)[16], float (&o)[G][8],
+                                             float& m_run, float& l_run) {
     constexpr int KST = HD / 32;        // 16x16x32 MFMA steps over head_dim
     constexpr int NC = HD / 8;          // 8-dim chunks (16 bytes) per row
     constexpr int KSL = 64 / NC;        // key slots per wave in the P.V phase
     constexpr int KPL = 16 / KSL;       // keys per slot per 16-key step
     static_assert(NC <= 64 && 16 % KSL == 0, "head_dim");
-
-    __shared__ float sP[4][16][16];     // per wave: p[key][head]
-    __shared__ float sAl[4][16];        // per wave: alpha[head]
-
-    const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int wid = blockIdx.x * 4 + wave;
-    if (wid >= a.B * a.n_kv * n_chunks) return;  // whole wave leaves; no block barriers below
-    const int ci = wid % n_chunks;
-    const int bg = wid / n_chunks;
-    const int g = bg % a.n_kv;
-    const int b = bg / a.n_kv;
-    const int L = a.pos0 + 1;
-    const int k_beg = ci * chunk;
-    const int k_end = min(L, k_beg + chunk);
-
+    const int bg = b * a.n_kv + g;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
 
     // Q fragments: B operand (column = head lane&15, dims 32kk + 8*(lane>>4) ..+8)
@@ -86,12 +77,12 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
 
     const int pc = lane % NC;   // P.V: dims 8*pc .. +8
     const int ps = lane / NC;   // P.V: key slot
-    float o[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
 
     // K and V of one 16-key step; the next step's loads are issued before the
     // current step is computed (two register buffers)
@@ -139,15 +130,15 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
         m_run = m_new;
         // ---- publish p and alpha to the wave's LDS slice
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sP[wave][4 * (lane >> 4) + r][hq] = s[r];
-        if (lane < 16) sAl[wave][lane] = alpha;
+        for (int r = 0; r < 4; ++r) sP[4 * (lane >> 4) + r][hq] = s[r];
+        if (lane < 16) sAl[lane] = alpha;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // ---- P.V on the vector ALU
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float al = sAl[wave][h];
+            const float al = sAl[h];
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[h][e] *= al;
         }
@@ -158,7 +149,7 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
             const int kl = ps * KPL + i;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float p = sP[wave][kl][h];
+                const float p = sP[kl][h];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[h][e] += p * v[e];
             }
@@ -167,14 +158,21 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
-    uint4 kfa[KST], vfa[KPL], kfb[KST], vfb[KPL];
-    load_step(k_beg, kfa, vfa);
-    for (int kt = k_beg; kt < k_end; kt += 32) {
-        if (kt + 16 < k_end) load_step(kt + 16, kfb, vfb);
-        step(kt, kfa, vfa);
-        if (kt + 16 < k_end) {
-            if (kt + 32 < k_end) load_step(kt + 32, kfa, vfa);
-            step(kt + 16, kfb, vfb);
+    // DEPTH register buffers: the loads of the next DEPTH-1 steps are in flight
+    // while a step is computed
+    uint4 kf[DEPTH][KST], vf[DEPTH][KPL];
+#pragma unroll
+    for (int d = 0; d + 1 < DEPTH; ++d)
+        if (k_beg + 16 * d < k_end) load_step(k_beg + 16 * d, kf[d], vf[d]);
+    for (int kt = k_beg; kt < k_end; kt += 16 * DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int kc = kt + 16 * d;
+            if (kc < k_end) {
+                const int kn = kc + 16 * (DEPTH - 1);
+                if (kn < k_end) load_step(kn, kf[(d + DEPTH - 1) % DEPTH], vf[(d + DEPTH - 1) % DEPTH]);
+                step(kc, kf[d], vf[d]);
+            }
         }
     }
 
@@ -186,6 +184,31 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], off, 64);
 
+}
+
+// Split over key chunks across workgroups (few units): one wave per chunk,
+// partials to ws, merged by attn_decode_merge_kernel.
+template <int HD, int G>
+__global__ void __launch_bounds__(256)
+attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part_o,
+                   float* __restrict__ part_ml) {
+    constexpr int NC = HD / 8;
+    __shared__ float sP[4][16][16];     // per wave: p[key][head]
+    __shared__ float sAl[4][16];        // per wave: alpha[head]
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wid = blockIdx.x * 4 + wave;
+    if (wid >= a.B * a.n_kv * n_chunks) return;  // whole wave leaves; no block barriers below
+    const int ci = wid % n_chunks;
+    const int bg = wid / n_chunks;
+    const int g = bg % a.n_kv;
+    const int b = bg / a.n_kv;
+    const int L = a.pos0 + 1;
+    const int k_beg = ci * chunk;
+    const int k_end = min(L, k_beg + chunk);
+    float o[G][8], m_run, l_run;
+    decode_chunk<HD, G, 2>(a, b, g, k_beg, k_end, sP[wave], sAl[wave], o, m_run, l_run);
+    const int pc = lane % NC;
     const size_t base = ((size_t)b * a.n_heads + (size_t)g * G) * n_chunks + ci;
     if (lane < NC) {
 #pragma unroll
@@ -198,6 +221,57 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
     if (lane < G) {
         part_ml[2 * (base + (size_t)lane * n_chunks) + 0] = m_run;
         part_ml[2 * (base + (size_t)lane * n_chunks) + 1] = l_run;
+    }
+}
+
+// One workgroup per unit (sequence b, KV head g) when there are enough units to
+// fill the GPU: AD_FW waves split the unit's keys into contiguous chunks and
+// their partial states are merged through LDS in wave order, so no partials
+// leave the workgroup and no second kernel is needed.
+constexpr int AD_FW = 8;
+
+template <int HD, int G>
+__global__ void __launch_bounds__(64 * AD_FW)
+attn_decode_fused_kernel(AttnArgs a) {
+    constexpr int NC = HD / 8;
+    __shared__ float sP[AD_FW][16][16];
+    __shared__ float sAl[AD_FW][16];
+    __shared__ float sO[AD_FW][G][HD];
+    __shared__ float sM[AD_FW][G], sL[AD_FW][G];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int g = blockIdx.x % a.n_kv;
+    const int b = blockIdx.x / a.n_kv;
+    const int L = a.pos0 + 1;
+    const int chunk = ((L + AD_FW - 1) / AD_FW + 15) / 16 * 16;
+    const int k_beg = min(L, wave * chunk);
+    const int k_end = min(L, k_beg + chunk);
+    float o[G][8], m_run, l_run;
+    decode_chunk<HD, G, (G <= 4 ? 3 : 2)>(a, b, g, k_beg, k_end, sP[wave], sAl[wave], o, m_run, l_run);
+    if (lane < NC) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sO[wave][h][8 * lane + e] = o[h][e];
+    }
+    if (lane < G) {
+        sM[wave][lane] = m_run;
+        sL[wave][lane] = l_run;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * HD; idx += 64 * AD_FW) {
+        const int h = idx / HD, j = idx % HD;
+        float mmax = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < AD_FW; ++w) mmax = fmaxf(mmax, sM[w][h]);
+        float den = 0.f, num = 0.f;
+#pragma unroll
+        for (int w = 0; w < AD_FW; ++w) {
+            const float wt = sL[w][h] > 0.f ? exp2f(sM[w][h] - mmax) : 0.f;  // empty chunks add nothing
+            den += wt * sL[w][h];
+            num += wt * sO[w][h][j];
+        }
+        ((bf16_t*)a.o)[((size_t)b * a.n_heads + (size_t)g * G + h) * HD + j] = f2bf(num / den);
     }
 }
 
@@ -238,9 +312,24 @@ size_t attn_decode_ws_bytes(int B, int n_heads, int n_kv, int hd, int n_keys) {
     return (size_t)B * n_heads * p.n_chunks * (hd + 2) * sizeof(float);
 }
 
+template <int G>
+hipError_t launch_fused(const AttnArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((attn_decode_fused_kernel<128, G>), dim3(a.B * a.n_kv), dim3(64 * AD_FW), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t attn_decode_bf16_launch(const AttnArgs& a, float* ws, hipStream_t s) {
     if (a.hd != 128 || a.n_kv <= 0 || a.n_heads % a.n_kv != 0 || a.B <= 0 || a.pos0 < 0)
         return hipErrorInvalidValue;
+    if (a.B * a.n_kv >= AD_FUSED_MIN_UNITS) {
+        switch (a.n_heads / a.n_kv) {
+            case 1: return launch_fused<1>(a, s);
+            case 2: return launch_fused<2>(a, s);
+            case 4: return launch_fused<4>(a, s);
+            case 8: return launch_fused<8>(a, s);
+            default: break;
+        }
+    }
     const int L = a.pos0 + 1;
     const DecodePlan p = plan_decode(a.B, a.n_kv, L);
     float* part_o = ws;

@@ -318,20 +318,22 @@ hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_
 int gemv_bf16_ssq_parts(int N) { return N / GV_BN; }
 
 // ---------------------------------------------------------------------------
-// RMSNorm operand: one wave per row.  a[m, j] = bf16(x[m, j] * g[j]) (one
-// rounding) and ssq[m] = sum_j x[m, j]^2 accumulated in fp32 across the wave
-// ("Llama 3.1 70B", section "RMSNorm": the reduction is done in fp32).  The
-// inverse RMS itself is applied to the fp32 results of the projection.
+// RMSNorm operand: one workgroup per row.  a[m, j] = bf16(x[m, j] * g[j]) (one
+// rounding) and ssq[m] = sum_j x[m, j]^2 accumulated in fp32 across the
+// workgroup ("Llama 3.1 70B", section "RMSNorm": the reduction is done in
+// fp32).  The inverse RMS itself is applied to the fp32 results of the
+// projection.
 __global__ void __launch_bounds__(256)
 norm_rows_kernel(const float* __restrict__ x, const float* __restrict__ g, bf16_t* __restrict__ a,
                  float* __restrict__ ssq, int M, int d) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ float s_red[4];
+    const int row = blockIdx.x;
     const int lane = threadIdx.x & 63;
-    if (row >= M) return;
     const float* xr = x + (size_t)row * d;
     bf16_t* ar = a + (size_t)row * d;
     float s = 0.f;
-    for (int j = lane * 8; j < d; j += 64 * 8) {
+#pragma unroll 4
+    for (int j = threadIdx.x * 8; j < d; j += 256 * 8) {
         const float4 v0 = *(const float4*)(xr + j);
         const float4 v1 = *(const float4*)(xr + j + 4);
         const float4 g0 = *(const float4*)(g + j);
@@ -346,14 +348,15 @@ norm_rows_kernel(const float* __restrict__ x, const float* __restrict__ g, bf16_
         *(uint4*)(ar + j) = p;
     }
     s = warp_sum(s);
-    if (lane == 0) ssq[row] = s;
+    if (lane == 0) s_red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) ssq[row] = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
 }
 
 hipError_t norm_rows_launch(const float* x, const float* g, void* a, float* ssq, int M, int d,
                             hipStream_t s) {
     if (M <= 0 || d % 8 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(norm_rows_kernel, dim3((M + 3) / 4), dim3(256), 0, s, x, g, (bf16_t*)a, ssq,
-                       M, d);
+    hipLaunchKernelGGL(norm_rows_kernel, dim3(M), dim3(256), 0, s, x, g, (bf16_t*)a, ssq, M, d);
     return hipGetLastError();
 }
 

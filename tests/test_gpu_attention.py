@@ -159,6 +159,8 @@ def _oracle_decode(q, kc, vc, P):
 @pytest.mark.parametrize("G,B,P", [
     (4, 1, 0), (4, 3, 1), (4, 2, 14), (4, 2, 15), (4, 2, 16), (4, 32, 1000),
     (8, 2, 4096), (1, 2, 200), (2, 3, 77), (8, 64, 129), (8, 1, 16383),
+    # >= 128 (sequence, KV head) units: one workgroup per unit, chunks merged in LDS
+    (4, 64, 300), (2, 64, 17), (1, 128, 40),
 ])
 def test_attention_decode_random(G, B, P):
     Hkv = 2
