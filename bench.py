@@ -77,7 +77,7 @@ def stage_bytes(wl):
 
 
 # ------------------------------------------------------------- GPU timing
-def time_workload(name, steps, warmup, sets=1):
+def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
     import torch
     import workloads
     from dense_decoder_only_amd import llb
@@ -92,6 +92,8 @@ def time_workload(name, steps, warmup, sets=1):
     x = workloads.make_x(wl.B, wl.T, shp.d_model, gen, device=dev)
     for i in range(sets):
         blocks.append(llb.llb_block_create(llb.make_config(shp, cap), w))
+        if tiles is not None:
+            llb.llb_block_set_tiles(blocks[-1], *tiles)
         kc, vc = workloads.make_cache(shp, wl.B, wl.P, cap, gen, device=dev)
         caches.append((kc, vc))
     del w
@@ -107,9 +109,17 @@ def time_workload(name, steps, warmup, sets=1):
         else:
             llb.llb_block_decode(blk, x, y, wl.B, wl.P, kc, vc, cap, ws)
 
-    for i in range(warmup):
-        step(i)
+    # At least `warmup` steps and at least `warm_seconds` of back-to-back work:
+    # the GPU's clocks take a few hundred milliseconds of load to settle.
+    t_warm = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - t_warm < warm_seconds:
+        step(n_warm)
+        n_warm += 1
+        if n_warm % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    log(f"{name}: {n_warm} warm-up steps")
     for b in blocks:
         llb.llb_block_set_stage_timing(b, True)
         llb.llb_block_stage_times(b)           # clear

@@ -211,26 +211,24 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 }
 
 // Picks the prefill tile configuration (see gemm_bf16.hip) of C[M,N] = A[M,K] W^T
-// from measurements of the whole block on MI355X:
+// from measurements of the whole block on MI355X (steady clocks):
 //  - long inputs (M >= 4096): 256x256 tiles; the interleaved 4-wave kernel for
-//    the long-K or wide projections, the 8-wave kernel otherwise;
-//  - 256x256 tiles filling at least 2 rounds of the 256 compute units: the
-//    interleaved kernel; at least 160 tiles: the 8-wave kernel;
-//  - otherwise 256x128 tiles: BK 64 with one workgroup per CU when there is
-//    about one tile per CU, BK 32 with two workgroups per CU beyond that.
+//    long K, the 8-wave kernel otherwise;
+//  - 256x192 tiles when they fill whole rounds of the 256 compute units;
+//  - 256x256 tiles (8-wave kernel) once they fill at least 160 compute units;
+//  - 256x128 tiles (interleaved, BK 64, 3 stages) from 192 tiles up when K is
+//    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that.
 int pick_tile(int M, int N, int K) {
     const int pm = (M + 255) / 256;
-    if (N % 256 == 0 && M >= 4096) return (K >= 16384 || N >= 32768) ? 3 : 0;
+    if (N % 256 == 0 && M >= 4096) return K >= 16384 ? 3 : 0;
     if (N % 128 != 0) return -1;
-    if (N % 256 == 0 && (long)pm * (N / 256) >= 512) return 3;
+    if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return 6;
     if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return 0;
     const long t128 = (long)pm * (N / 128);
-    if (t128 >= 512) return 1;
-    if (t128 >= 192 && K % 64 == 0) return 5;
+    if (t128 >= 192 && K % 64 == 0) return 7;
     return M > 128 ? 1 : 2;
 }
 
-// Prefill tile configuration of a bf16 projection (-1 if none fits N).
 int tile_for(const llb_block* b, int override_cfg, int M, int N, int K) {
     (void)b;
     return override_cfg >= 0 ? override_cfg : pick_tile(M, N, K);
@@ -277,6 +275,22 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     const bool bf16 = c.wdtype == LLB_BF16;
     const bool small_m = decode && M <= 64;
     const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * hd;
+    const int tile_qkv = tile_for(b, b->tile_qkv, M, nqkv, d);
+    const int tile_o = tile_for(b, b->tile_o, M, d, c.n_heads * hd);
+    const int tile_gu = tile_for(b, b->tile_gu, M, 2 * c.d_ff, d);
+    const int tile_down = tile_for(b, b->tile_down, M, d, c.d_ff);
+    if (bf16 && !small_m) {
+        // every projection's tile fits before anything is queued
+        const struct { int cfg, N, K, epi; const char* what; } chk[] = {
+            {tile_qkv, nqkv, d, llb::EPI_QKV, "qkv projection"},
+            {tile_o, d, c.n_heads * hd, llb::EPI_RESID_NORM, "output projection"},
+            {tile_gu, 2 * c.d_ff, d, llb::EPI_SWIGLU, "gate/up projection"},
+            {tile_down, d, c.d_ff, llb::EPI_RESID, "down projection"}};
+        for (const auto& k : chk)
+            if (!llb::gemm_bf16_supports(k.cfg, k.N, k.K, k.epi))
+                return fail(LLB_E_UNSUPPORTED, "%s: tile configuration %d does not fit N=%d K=%d", k.what,
+                            k.cfg, k.N, k.K);
+    }
 
     llb::Epilogue e{};
     e.rope = b->rope;
@@ -296,8 +310,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = x; a.gain = b->g1; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_QKV; a.epi.q_out = q; a.epi.k_cache = kc; a.epi.v_cache = vc;
-    llb_status st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_qkv, M, nqkv, d), s,
-                             "qkv projection");
+    llb_status st = run_proj(b, a, small_m, scratch, tile_qkv, s, "qkv projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -313,7 +326,6 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
     // 3. h = x + O . Wo^T   (bf16: also the FFN RMSNorm's operand and row sums of h^2)
-    const int tile_o = tile_for(b, b->tile_o, M, d, c.n_heads * c.head_dim);
     a = llb::GemmArgs{};
     a.A = o; a.W = b->wo; a.M = M; a.N = d; a.K = c.n_heads * hd; a.eps = c.eps;
     a.epi = e; a.epi.resid = x; a.epi.out = h;
@@ -344,8 +356,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = h; a.gain = b->g2; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
-    st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_gu, M, 2 * c.d_ff, d), s,
-                  "gate/up projection");
+    st = run_proj(b, a, small_m, scratch, tile_gu, s, "gate/up projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -353,7 +364,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     a = llb::GemmArgs{};
     a.A = u; a.W = b->wdown; a.M = M; a.N = d; a.K = c.d_ff; a.eps = c.eps;
     a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = h; a.epi.out = y;
-    st = run_proj(b, a, small_m, scratch, tile_for(b, b->tile_down, M, d, c.d_ff), s, "down projection");
+    st = run_proj(b, a, small_m, scratch, tile_down, s, "down projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
     return LLB_OK;
@@ -592,6 +603,30 @@ llb_status llb_attention_decode(const llb_block* b, const void* q, const void* k
                        ? llb::attn_f32_launch(at, (hipStream_t)stream)
                        : llb::attn_decode_bf16_launch(at, (float*)ws, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attention decode");
+    return LLB_OK;
+}
+
+int32_t llb_gemm_num_tiles(void) { return llb::gemm_bf16_num_tile_cfgs(); }
+
+llb_status llb_gemm_tile_info(int32_t cfg, int32_t* bm, int32_t* bn) {
+    if (cfg < 0 || cfg >= llb::gemm_bf16_num_tile_cfgs()) return fail(LLB_E_INVALID, "no tile configuration %d", cfg);
+    if (!bm || !bn) return fail(LLB_E_INVALID, "output pointer is NULL");
+    int m, n, t;
+    llb::gemm_bf16_tile(cfg, &m, &n, &t);
+    *bm = m;
+    *bn = n;
+    return LLB_OK;
+}
+
+llb_status llb_block_set_tiles(llb_block* b, int32_t qkv, int32_t o, int32_t gate_up, int32_t down) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    const int n = llb::gemm_bf16_num_tile_cfgs();
+    for (int32_t v : {qkv, o, gate_up, down})
+        if (v < -1 || v >= n) return fail(LLB_E_INVALID, "tile configuration %d outside [-1, %d)", v, n);
+    b->tile_qkv = qkv;
+    b->tile_o = o;
+    b->tile_gu = gate_up;
+    b->tile_down = down;
     return LLB_OK;
 }
 

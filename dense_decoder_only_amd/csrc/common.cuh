@@ -71,6 +71,13 @@ LLB_DEV float warp_max(float v) {
 
 LLB_DEV float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
+// SiLU for bf16 results: the hardware exp2 and reciprocal (about 1 ulp each in
+// fp32, far below bf16's half-ulp of 2^-9).  Large |z| behave: exp2 -> inf
+// gives 0 (z < 0), exp2 -> 0 gives z (z > 0).
+LLB_DEV float silu_bf16(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
 // Inverse RMS of a row from its fp32 sum of squares (eps inside the square root).
 LLB_DEV float inv_rms(float sumsq, int n, float eps) {
     return 1.0f / sqrtf(sumsq / (float)n + eps);

@@ -13,6 +13,8 @@
 //             ("Llama 3.1 70B", section "SwiGLU MLP").
 #pragma once
 
+#include <type_traits>
+
 #include "common.cuh"
 #include "kernels.h"
 
@@ -69,7 +71,10 @@ LLB_DEV void epi_norm_operand(const Epilogue& e, int m, int n, int N, float h) {
 // gate = C[m, 64*grp + j], up = C[m, 64*grp + 32 + j]; feature f = 32*grp + j.
 template <typename OT>
 LLB_DEV void epi_swiglu(const Epilogue& e, int m, int f, int d_ff, float gate, float up) {
-    store_elem<OT>(e.u_out, (size_t)m * d_ff + f, silu_f(gate) * up);
+    if constexpr (std::is_same<OT, bf16_t>::value)
+        store_elem<OT>(e.u_out, (size_t)m * d_ff + f, silu_bf16(gate) * up);
+    else
+        store_elem<OT>(e.u_out, (size_t)m * d_ff + f, silu_f(gate) * up);
 }
 
 // ---- 8-column forms: v[0..7] = C[m, n..n+7], n a multiple of 8 -------------
@@ -141,7 +146,7 @@ LLB_DEV void epi_swiglu8(const Epilogue& e, int m, int f, int d_ff, const float*
                          const float* up) {
     float u[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) u[k] = silu_f(gate[k]) * up[k];
+    for (int k = 0; k < 8; ++k) u[k] = silu_bf16(gate[k]) * up[k];
     *(uint4*)((bf16_t*)e.u_out + (size_t)m * d_ff + f) = pack8(u);
 }
 

@@ -87,9 +87,7 @@ gemm_bf16_kernel(GemmArgs args) {
     // fragment reads and MFMAs, with latency hidden by the other waves of the
     // SIMD) and SCHED_INTERLEAVE (one wave per SIMD, its LDS reads and copies
     // threaded between its MFMAs).
-    static_assert(SCHED != SCHED_INTERLEAVE ||
-                      (NW == 4 && TM == 4 && TN == 4 && (BK == 32 || BK == 64) && STAGES >= 2 &&
-                       L <= 8 * (BK / 16 - 1)),
+    static_assert(SCHED != SCHED_INTERLEAVE || (NW == 4 && (BK == 32 || BK == 64) && STAGES >= 2),
                   "interleaved shape");
     const int wm = wave % WAVES_M;
     const int wn = wave / WAVES_M;
@@ -207,15 +205,19 @@ gemm_bf16_kernel(GemmArgs args) {
                 if (kt + st < nk) step(kt + st, st, (st + STAGES - 1) % STAGES);
         }
     } else {
-        // Interleaved: one wave per SIMD owns a 128x128 block.  Within k-tile t
-        // (two k-steps of 16), the 16 MFMAs of step 0 are threaded with the
-        // LDS reads of step 1's fragments and the copies of k-tile t+STAGES-1
-        // into the stage of k-tile t-1; the 16 MFMAs of step 1 are split around the
-        // wait + barrier that publishes k-tile t+1, after which step 0's
-        // fragments of k-tile t+1 are read between the last 8 MFMAs.  Every
-        // element is pinned in place with a scheduling barrier.
-        bf16x8 fa[2][TM], fb[2][TN];
+        // Interleaved: one wave per SIMD owns a WTM x WTN block (TM x TN MFMA
+        // blocks, NM = TM*TN MFMAs per k-step of 16, NR = TM+TN fragment
+        // reads).  Within k-tile t, the MFMAs of steps 0..KS-2 are threaded with
+        // the reads of the next step's fragments (first) and this k-tile's share
+        // of the copies of k-tile t+STAGES-1 into the stage of k-tile t-1; the
+        // MFMAs of the last step are split around the wait + barrier that
+        // publishes k-tile t+1, after which step 0's fragments of k-tile t+1 are
+        // read between the remaining MFMAs.  Every element is pinned in place
+        // with a scheduling barrier.
+        constexpr int NM = TM * TN, NR = TM + TN;
         constexpr int KS = BK / 16;
+        static_assert(NR <= NM, "reads ride on the MFMAs");
+        bf16x8 fa[2][TM], fb[2][TN];
         uint32_t a_off[KS], b_off[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -232,14 +234,14 @@ gemm_bf16_kernel(GemmArgs args) {
         auto rd_b = [&](int st, int kk, int fbuf, int j) {
             fb[fbuf][j] = *(lds_frag_ptr)(uintptr_t)(b_off[kk] + st * STAGE_BYTES + j * 32 * BK * 2);
         };
-        // n-th of the 8 fragment reads, in the order the MFMAs (i-major) first
-        // use them: A0 B0 B1 B2 B3 A1 A2 A3
+        // n-th of the NR fragment reads, in the order the MFMAs (i-major) first
+        // use them: A0 B0 .. B(TN-1) A1 .. A(TM-1)
         auto rd = [&](int st, int kk, int fbuf, int n) {
             if (n == 0) rd_a(st, kk, fbuf, 0);
             else if (n <= TN) rd_b(st, kk, fbuf, n - 1);
             else rd_a(st, kk, fbuf, n - TN);
         };
-        auto mf = [&](int fbuf, int n) {  // n-th of the 16 MFMAs of a k-step
+        auto mf = [&](int fbuf, int n) {  // n-th of the NM MFMAs of a k-step
             const int i = n / TN, j = n % TN;
             acc[i][j] = mfma32(fa[fbuf][i], fb[fbuf][j], acc[i][j]);
         };
@@ -254,7 +256,10 @@ gemm_bf16_kernel(GemmArgs args) {
         wait_vm_lgkm<(STAGES - 2) * L>();
         barrier();
 #pragma unroll
-        for (int n = 0; n < 8; ++n) rd(0, 0, 0, n);
+        for (int n = 0; n < NR; ++n) rd(0, 0, 0, n);
+        // copies per step of 0..KS-2 (the last step carries none)
+        constexpr int CPS = KS > 1 ? (L + KS - 2) / (KS - 1) : L;
+        constexpr int HALF = NM / 2;
         // The body is the same for every k-tile: near the end, the copies of
         // "k-tile t+STAGES-1" repeat the last k-tile into the free stage and
         // the reads of "k-tile t+1" land in registers that are not used again.
@@ -262,23 +267,30 @@ gemm_bf16_kernel(GemmArgs args) {
             const int t_copy = min(t + STAGES - 1, nk - 1);
             const int st_copy = (st + STAGES - 1) % STAGES;
             const int st_next = (st + 1) % STAGES;
-            // steps 0..KS-2: 16 MFMAs each; the 8 reads of the next step ride
-            // on the first 8, this k-tile's share of the copies on the last 8
 #pragma unroll
             for (int ks = 0; ks + 1 < KS; ++ks) {
+                // ops of this step: NR reads, then copies ks*CPS .. ks*CPS+CPS-1
+                constexpr int Q = NR + CPS;
 #pragma unroll
-                for (int n = 0; n < 16; ++n) {
+                for (int n = 0; n < NM; ++n) {
                     mf(ks & 1, n);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (n < 8) rd(st, ks + 1, (ks + 1) & 1, n);
-                    else if (ks * 8 + n - 8 < L) dma_one(t_copy, st_copy, ks * 8 + n - 8);
+#pragma unroll
+                    for (int q = n * Q / NM; q < (n + 1) * Q / NM; ++q) {
+                        if (q < NR) rd(st, ks + 1, (ks + 1) & 1, q);
+                        else if (ks * CPS + q - NR < L) dma_one(t_copy, st_copy, ks * CPS + q - NR);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            }
+            if constexpr (KS == 1) {
+#pragma unroll
+                for (int i = 0; i < L; ++i) dma_one(t_copy, st_copy, i);
             }
             constexpr int LB = (KS - 1) & 1;  // fragment buffer of the last step
             // last step, first half
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
+            for (int n = 0; n < HALF; ++n) {
                 mf(LB, n);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -287,10 +299,12 @@ gemm_bf16_kernel(GemmArgs args) {
             barrier();
             // last step, second half, with step 0's fragments of k-tile t+1
 #pragma unroll
-            for (int n = 8; n < 16; ++n) {
+            for (int n = HALF; n < NM; ++n) {
                 mf(LB, n);
                 __builtin_amdgcn_sched_barrier(0);
-                rd(st_next, 0, 0, n - 8);
+#pragma unroll
+                for (int q = (n - HALF) * NR / (NM - HALF); q < (n - HALF + 1) * NR / (NM - HALF); ++q)
+                    rd(st_next, 0, 0, q);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -420,15 +434,29 @@ constexpr TileCfg kTiles[] = {
     {256, 256, 2, 2, 64, 2, 1, 1},  // 4 waves (1 per SIMD), wave tile 128x128, interleaved, BK 64
     {256, 256, 2, 2, 32, 4, 1, 1},  // the same with BK 32 and 4 stages
     {256, 128, 2, 2, 64, 3, 1, 0},  // 4 waves, BK 64, 3 stages (144 KB)
+    {256, 192, 2, 2, 64, 2, 1, 1},  // interleaved, wave tile 128x96 (N = 6144: 256 tiles at M = 2048)
+    {256, 128, 2, 2, 64, 3, 1, 1},  // interleaved, wave tile 128x64, 3 stages
+    {256, 256, 2, 2, 32, 5, 1, 1},  // interleaved 128x128, BK 32, 5 stages (160 KB)
+    {256, 192, 2, 2, 32, 5, 1, 1},  // interleaved 128x96, BK 32, 5 stages (140 KB)
+    {256, 128, 2, 2, 32, 5, 1, 1},  // interleaved 128x64, BK 32, 5 stages (120 KB)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 template <int BM, int BN, int WM, int WN, int BK, int ST, int OCC, int SCHED, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
-    const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, ST, OCC, EPI, SCHED>), dim3(tiles),
-                       dim3(64 * WM * WN), 0, s, a);
-    return hipGetLastError();
+    // a wave's column slice must hold whole (gate, up) 64-column pairs for
+    // SwiGLU, and a power-of-two number of 8-column chunks (8 or 16) for the
+    // norm-operand row reduction; other shapes reject those epilogues
+    constexpr int WTN = BN / WN;
+    if constexpr ((EPI == EPI_SWIGLU && WTN % 64 != 0) ||
+                  (EPI == EPI_RESID_NORM && WTN != 64 && WTN != 128)) {
+        return hipErrorInvalidValue;
+    } else {
+        const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, ST, OCC, EPI, SCHED>), dim3(tiles),
+                           dim3(64 * WM * WN), 0, s, a);
+        return hipGetLastError();
+    }
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int ST, int OCC, int SCHED = SCHED_PLAIN>
@@ -454,6 +482,16 @@ hipError_t tile_weights_launch(const void* src, void* dst, int N, int K, hipStre
     return hipGetLastError();
 }
 
+bool gemm_bf16_supports(int cfg, int N, int K, int epi) {
+    if (cfg < 0 || cfg >= kNumTiles) return false;
+    const TileCfg t = kTiles[cfg];
+    if (N <= 0 || N % t.bn != 0 || K < t.bk || K % t.bk != 0) return false;
+    const int wtn = t.bn / t.wn;
+    if (epi == EPI_SWIGLU && wtn % 64 != 0) return false;
+    if (epi == EPI_RESID_NORM && wtn != 64 && wtn != 128) return false;
+    return true;
+}
+
 void gemm_bf16_tile(int cfg, int* bm, int* bn, int* threads) {
     *bm = kTiles[cfg].bm;
     *bn = kTiles[cfg].bn;
@@ -462,15 +500,19 @@ void gemm_bf16_tile(int cfg, int* bm, int* bn, int* threads) {
 
 hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
     if (cfg < 0 || cfg >= kNumTiles) return hipErrorInvalidValue;
-    const TileCfg t = kTiles[cfg];
-    if (a.M <= 0 || a.N % t.bn != 0 || a.K % t.bk != 0 || a.K / t.bk < 1) return hipErrorInvalidValue;
+    if (a.M <= 0 || !gemm_bf16_supports(cfg, a.N, a.K, a.epi.kind)) return hipErrorInvalidValue;
     switch (cfg) {
         case 0: return launch_cfg<256, 256, 4, 2, 64, 2, 2>(a, s);
         case 1: return launch_cfg<256, 128, 2, 2, 32, 3, 2>(a, s);
         case 2: return launch_cfg<128, 128, 2, 2, 32, 4, 2>(a, s);
         case 3: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_INTERLEAVE>(a, s);
         case 4: return launch_cfg<256, 256, 2, 2, 32, 4, 1, SCHED_INTERLEAVE>(a, s);
-        default: return launch_cfg<256, 128, 2, 2, 64, 3, 1>(a, s);
+        case 5: return launch_cfg<256, 128, 2, 2, 64, 3, 1>(a, s);
+        case 6: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_INTERLEAVE>(a, s);
+        case 7: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_INTERLEAVE>(a, s);
+        case 8: return launch_cfg<256, 256, 2, 2, 32, 5, 1, SCHED_INTERLEAVE>(a, s);
+        case 9: return launch_cfg<256, 192, 2, 2, 32, 5, 1, SCHED_INTERLEAVE>(a, s);
+        default: return launch_cfg<256, 128, 2, 2, 32, 5, 1, SCHED_INTERLEAVE>(a, s);
     }
 }
 

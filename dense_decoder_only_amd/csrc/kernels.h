@@ -58,6 +58,10 @@ struct GemmArgs {
 // Large-M projection (prefill): LDS-staged bf16 MFMA tiles.
 hipError_t gemm_bf16_launch(const GemmArgs& a, int tile_cfg, hipStream_t s);
 // Tile configurations available to gemm_bf16_launch: returns BM, BN, threads.
+// Whether tile configuration cfg can run C[M, N] = A[M, K] W^T with epilogue
+// kind epi (BN divides N, BK divides K, the per-wave column slice holds the
+// epilogue's column groups).
+bool gemm_bf16_supports(int cfg, int N, int K, int epi);
 void gemm_bf16_tile(int tile_cfg, int* bm, int* bn, int* threads);
 int gemm_bf16_num_tile_cfgs();
 // The bf16 projections read W in 128-row x 64-column tiles: element (n, k) of

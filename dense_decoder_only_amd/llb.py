@@ -32,7 +32,8 @@ STATUS_NAMES = {0: "LLB_OK", -1: "LLB_E_INVALID", -2: "LLB_E_UNSUPPORTED", -3: "
 EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes",
             "llb_block_prefill", "llb_block_decode", "llb_kv_append", "llb_attention_prefill",
             "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
-            "llb_block_stage_times", "llb_last_error")
+            "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles",
+            "llb_last_error")
 
 STAGES = ("qkv", "attention", "o_proj", "gate_up", "down")
 
@@ -95,6 +96,12 @@ def load_library(path: str = LIB_PATH):
     lib.llb_block_set_stage_timing.restype = ctypes.c_int
     lib.llb_block_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
     lib.llb_block_stage_times.restype = ctypes.c_int
+    lib.llb_gemm_num_tiles.argtypes = []
+    lib.llb_gemm_num_tiles.restype = i32
+    lib.llb_gemm_tile_info.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.llb_gemm_tile_info.restype = ctypes.c_int
+    lib.llb_block_set_tiles.argtypes = [vp, i32, i32, i32, i32]
+    lib.llb_block_set_tiles.restype = ctypes.c_int
     lib.llb_last_error.argtypes = []
     lib.llb_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -205,6 +212,21 @@ def llb_attention_decode(blk: Block, q, k_cache, v_cache, o, B, start_pos, cache
                                                _ptr(o), B, start_pos, cache_cap, _ptr(ws),
                                                ws.numel() * ws.element_size(), _stream(stream)),
            "llb_attention_decode")
+
+
+def llb_gemm_num_tiles() -> int:
+    return int(load_library().llb_gemm_num_tiles())
+
+
+def llb_gemm_tile_info(cfg: int):
+    """(BM, BN) of prefill tile configuration `cfg`."""
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().llb_gemm_tile_info(cfg, ctypes.byref(bm), ctypes.byref(bn)), "llb_gemm_tile_info")
+    return int(bm.value), int(bn.value)
+
+
+def llb_block_set_tiles(blk: Block, qkv: int = -1, o: int = -1, gate_up: int = -1, down: int = -1) -> None:
+    _check(load_library().llb_block_set_tiles(blk.handle, qkv, o, gate_up, down), "llb_block_set_tiles")
 
 
 def llb_block_set_stage_timing(blk: Block, enable: bool) -> None:

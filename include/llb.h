@@ -168,6 +168,24 @@ size_t llb_attention_workspace_bytes(const llb_block* blk, int32_t B, int32_t n_
 llb_status llb_block_set_stage_timing(llb_block* blk, int32_t enable);
 llb_status llb_block_stage_times(llb_block* blk, float* ms, int32_t* n_calls);
 
+/* Tuning and test hooks for the bf16 prefill projections.  The library holds
+ * a fixed table of GEMM tile configurations (workgroup tile BM x BN, waves,
+ * k-depth, pipeline stages, schedule); by default each projection picks one
+ * from M, N and K.  llb_gemm_tile_info writes configuration `cfg`'s tile rows
+ * and columns to *bm and *bn (LLB_E_INVALID if cfg is outside
+ * [0, llb_gemm_num_tiles())).  llb_block_set_tiles fixes the configuration of
+ * the QKV, output, gate/up and down projections of later calls on `blk` that
+ * run them as GEMMs: prefill calls, and decode calls over more than 64
+ * sequences (smaller decode batches use the weight-streaming kernels); fp32
+ * blocks ignore it.  -1 restores the automatic choice; values outside
+ * [-1, count) give LLB_E_INVALID and change nothing.  A call whose
+ * configuration for some projection has a BN that does not divide that
+ * projection's N, or a per-wave column slice that cannot hold its fused
+ * epilogue, fails with LLB_E_UNSUPPORTED before any work is queued. */
+int32_t llb_gemm_num_tiles(void);
+llb_status llb_gemm_tile_info(int32_t cfg, int32_t* bm, int32_t* bn);
+llb_status llb_block_set_tiles(llb_block* blk, int32_t qkv, int32_t o, int32_t gate_up, int32_t down);
+
 /* Thread-local text describing the last non-OK status ("" if none). */
 const char* llb_last_error(void);
 

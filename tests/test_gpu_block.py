@@ -102,6 +102,76 @@ def test_bf16_prefill_small(d, H, Hkv, dff, B, T, scaled):
     assert torch.all(kd[:, :, T:].float() == SENTINEL)
 
 
+# Every prefill GEMM tile configuration on every projection whose N its BN
+# divides: d = 1536 and 2 d_ff = 1536 are multiples of 768 = lcm(128, 192, 256),
+# QKV N = 24 heads x 128 = 3072 as well; M = 300 leaves a ragged second row tile.
+TILE_SHAPE = dict(d_model=1536, n_heads=16, n_kv_heads=4, head_dim=128, d_ff=768)
+
+
+@pytest.mark.parametrize("cfg", range(12))
+def test_bf16_prefill_every_tile_config(cfg):
+    from dense_decoder_only_amd import llb
+    n = llb.llb_gemm_num_tiles()
+    if cfg >= n:
+        pytest.skip(f"the library has {n} tile configurations")
+    bm, bn = llb.llb_gemm_tile_info(cfg)
+    shp = shape(**TILE_SHAPE, rope_scaling=False)
+    B, T = 1, 300
+    cap = workloads.cache_capacity(T)
+    w, x, kc, vc = gen_inputs(shp, 900 + cfg, B, T, 0, cap, fill=SENTINEL)
+    y_ref, k_ref, v_ref = oracle.block_forward(shp, w, x, kc, vc, 0)
+    nqkv = (shp.n_heads + 2 * shp.n_kv_heads) * shp.head_dim
+    Ns = {"qkv": nqkv, "o": shp.d_model, "gate_up": 2 * shp.d_ff, "down": shp.d_model}
+    gb = GpuBlock(shp, w, max_positions=cap)
+    ran = []
+    try:
+        for proj, N in Ns.items():
+            llb.llb_block_set_tiles(gb.blk, **{proj: cfg})
+            note(f"tile config {cfg} ({bm}x{bn}) on the {proj} projection (N={N})")
+            kd, vd = kc.cuda(), vc.cuda()
+            try:
+                y = gb.prefill(x.cuda(), kd, vd)
+                torch.cuda.synchronize()
+            except llb.LlbError as err:
+                # refused before any work: BN does not divide N, or the per-wave
+                # slice cannot hold a fused epilogue (SwiGLU pairs, norm sums)
+                assert err.status == llb.LLB_E_UNSUPPORTED, str(err)
+                assert N % bn != 0 or proj in ("o", "gate_up"), str(err)
+                note(f"  refused: {err}")
+                continue
+            finally:
+                llb.llb_block_set_tiles(gb.blk)
+            assert N % bn == 0
+            y, kd, vd = y.cpu(), kd.cpu(), vd.cpu()
+            e_y = rel_err(y, y_ref)
+            e_k = bf16_err(kd[:, :, :T], k_ref)
+            e_v = bf16_err(vd[:, :, :T], v_ref)
+            note(f"  y {e_y:.2e}  k {e_k:.3f}  v {e_v:.3f}")
+            assert e_y <= 2e-2 and e_k <= 1.0 and e_v <= 1.0
+            assert torch.all(kd[:, :, T:].float() == SENTINEL)
+            ran.append(proj)
+    finally:
+        gb.close()
+    assert ran, "no projection accepted the configuration"
+
+
+def test_tile_override_rejects_bad_values():
+    from dense_decoder_only_amd import llb
+    shp = shape(**TILE_SHAPE, rope_scaling=False)
+    w, _, _, _ = gen_inputs(shp, 5, 1, 1, 0, 16)
+    gb = GpuBlock(shp, w, max_positions=16)
+    try:
+        n = llb.llb_gemm_num_tiles()
+        for bad in (-2, n):
+            with pytest.raises(llb.LlbError) as ei:
+                llb.llb_block_set_tiles(gb.blk, qkv=bad)
+            assert ei.value.status == llb.LLB_E_INVALID
+        with pytest.raises(llb.LlbError):
+            llb.llb_gemm_tile_info(n)
+    finally:
+        gb.close()
+
+
 @pytest.mark.parametrize("B,P,G", [(5, 300, 4), (40, 64, 4), (70, 20, 4), (2, 1000, 8), (1, 0, 4)])
 def test_bf16_decode_small(B, P, G):
     Hkv = 2
