@@ -58,6 +58,7 @@ struct llb_block {
     float* g2;       // FFN RMSNorm gain, fp32 [d]
     float2* rope;    // [max_positions][hd/2] (cos, sin)
     int tile_qkv, tile_o, tile_gu, tile_down;  // bf16 prefill tile choice per projection (-1 = pick by M)
+    int num_cus;                     // compute units of the device
     int timing;                      // record stage events on every call
     std::vector<hipEvent_t> events;  // 6 per recorded call
     size_t events_used;
@@ -212,15 +213,15 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 
 // Picks the prefill tile configuration (see gemm_bf16.hip) of C[M,N] = A[M,K] W^T
 // from measurements of the whole block on MI355X (steady clocks):
-//  - long inputs (M >= 4096): 256x256 tiles; the interleaved 4-wave kernel for
-//    long K, the 8-wave kernel otherwise;
+//  - long inputs (M >= 4096): 256x256 tiles; the interleaved 4-wave kernel
+//    with the L2 prefetch for long K or wide N, the 8-wave kernel otherwise;
 //  - 256x192 tiles when they fill whole rounds of the 256 compute units;
 //  - 256x256 tiles (8-wave kernel) once they fill at least 160 compute units;
 //  - 256x128 tiles (interleaved, BK 64, 3 stages) from 192 tiles up when K is
 //    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that.
 int pick_tile(int M, int N, int K) {
     const int pm = (M + 255) / 256;
-    if (N % 256 == 0 && M >= 4096) return K >= 16384 ? 3 : 0;
+    if (N % 256 == 0 && M >= 4096) return (K >= 16384 || N >= 32768) ? 4 : 0;
     if (N % 128 != 0) return -1;
     if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return 6;
     if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return 0;
@@ -234,8 +235,32 @@ int tile_for(const llb_block* b, int override_cfg, int M, int N, int K) {
     return override_cfg >= 0 ? override_cfg : pick_tile(M, N, K);
 }
 
+// The 256x128 interleaved configuration that takes over a projection's last,
+// partly filled round of 256-wide tiles.
+constexpr int kTailCfg = 7;
+
+// First output column of the tail of C[M, N] = A W^T under configuration cfg:
+// when 256-wide tiles fill r >= 1 whole rounds of the compute units and leave
+// the next round at most half full, the columns of the whole rounds keep cfg
+// and the rest run as 256x128 tiles, which fill that last round twice as
+// densely at half the length per tile.  0 = no split.
+int tail_split(const llb_block* b, int cfg, const llb::GemmArgs& a) {
+    int bm, bn, nt;
+    llb::gemm_bf16_tile(cfg, &bm, &bn, &nt);
+    int tbm, tbn;
+    llb::gemm_bf16_tile(kTailCfg, &tbm, &tbn, &nt);
+    if (bn != 256 || bm != tbm || a.epi.kind == llb::EPI_RESID_NORM ||
+        !llb::gemm_bf16_supports(kTailCfg, a.N, a.K, a.epi.kind))
+        return 0;
+    const long pm = (a.M + bm - 1) / bm;
+    const long tiles = pm * (a.N / bn);
+    const long rounds = tiles / b->num_cus, rem = tiles % b->num_cus;
+    if (rounds < 1 || rem == 0 || rem > b->num_cus / 2 || (rounds * b->num_cus) % pm != 0) return 0;
+    return (int)(rounds * b->num_cus / pm) * bn;
+}
+
 llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, float* scratch,
-                    int tile, hipStream_t s, const char* what) {
+                    int tile, bool auto_tile, hipStream_t s, const char* what) {
     hipError_t e;
     if (b->cfg.wdtype == LLB_F32) {
         e = llb::gemm_f32_launch(a, s);
@@ -244,7 +269,18 @@ llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, fl
         e = llb::gemv_bf16_launch(a, sp, scratch, s);
     } else {
         if (tile < 0) return fail(LLB_E_UNSUPPORTED, "%s: no tile fits N=%d", what, a.N);
-        e = llb::gemm_bf16_launch(a, tile, s);
+        const int split = auto_tile ? tail_split(b, tile, a) : 0;
+        if (split > 0) {
+            llb::GemmArgs head = a, tail = a;
+            head.n_begin = 0;
+            head.n_end = split;
+            tail.n_begin = split;
+            tail.n_end = a.N;
+            e = llb::gemm_bf16_launch(head, tile, s);
+            if (e == hipSuccess) e = llb::gemm_bf16_launch(tail, kTailCfg, s);
+        } else {
+            e = llb::gemm_bf16_launch(a, tile, s);
+        }
     }
     if (e != hipSuccess) return hip_fail(e, what);
     return LLB_OK;
@@ -310,7 +346,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = x; a.gain = b->g1; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_QKV; a.epi.q_out = q; a.epi.k_cache = kc; a.epi.v_cache = vc;
-    llb_status st = run_proj(b, a, small_m, scratch, tile_qkv, s, "qkv projection");
+    llb_status st = run_proj(b, a, small_m, scratch, tile_qkv, b->tile_qkv < 0, s, "qkv projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -343,7 +379,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     } else {
         a.epi.kind = llb::EPI_RESID;
     }
-    st = run_proj(b, a, small_m, scratch, tile_o, s, "output projection");
+    st = run_proj(b, a, small_m, scratch, tile_o, b->tile_o < 0, s, "output projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -356,7 +392,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = h; a.gain = b->g2; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
-    st = run_proj(b, a, small_m, scratch, tile_gu, s, "gate/up projection");
+    st = run_proj(b, a, small_m, scratch, tile_gu, b->tile_gu < 0, s, "gate/up projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -364,7 +400,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     a = llb::GemmArgs{};
     a.A = u; a.W = b->wdown; a.M = M; a.N = d; a.K = c.d_ff; a.eps = c.eps;
     a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = h; a.epi.out = y;
-    st = run_proj(b, a, small_m, scratch, tile_down, s, "down projection");
+    st = run_proj(b, a, small_m, scratch, tile_down, b->tile_down < 0, s, "down projection");
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
     return LLB_OK;
@@ -397,6 +433,11 @@ llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* s
     b->events_used = 0;
     hipError_t e = hipGetDevice(&b->device);
     if (e != hipSuccess) { delete b; return hip_fail(e, "hipGetDevice"); }
+    e = hipDeviceGetAttribute(&b->num_cus, hipDeviceAttributeMultiprocessorCount, b->device);
+    if (e != hipSuccess || b->num_cus <= 0) {
+        delete b;
+        return hip_fail(e != hipSuccess ? e : hipErrorInvalidDevice, "compute unit count");
+    }
 
     const size_t es = b->es, d = c.d_model, hd = c.head_dim, dff = c.d_ff;
     const size_t nq = (size_t)c.n_heads * hd, nkv = (size_t)c.n_kv_heads * hd;

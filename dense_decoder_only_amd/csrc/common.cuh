@@ -104,6 +104,15 @@ LLB_DEV void dma16(const void* gptr, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// Four bytes per lane from gptr into LDS at lds + 4 * lane (one 256-byte
+// block per wave), counted by vmcnt like dma16.
+LLB_DEV void dma4(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
 LLB_DEV uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
 }

@@ -41,7 +41,12 @@ LLB_DEV int swz(int r) {
     else return (r >> 1) & 7;
 }
 
-constexpr int SCHED_PLAIN = 0, SCHED_INTERLEAVE = 1;
+// Main-loop schedules: SCHED_PLAIN (per k-tile: wait, barrier, copies,
+// fragment reads and MFMAs, with latency hidden by the other waves of the
+// SIMD), SCHED_INTERLEAVE (one wave per SIMD, its LDS reads and copies
+// threaded between its MFMAs) and SCHED_INTERLEAVE_PF (the same, plus an L2
+// prefetch of the operand lines two k-tiles ahead of the copies).
+constexpr int SCHED_PLAIN = 0, SCHED_INTERLEAVE = 1, SCHED_INTERLEAVE_PF = 2;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OCC, int EPI, int SCHED>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(OCC)))
@@ -58,14 +63,19 @@ gemm_bf16_kernel(GemmArgs args) {
     constexpr int L = BLOCKS / NW;            // DMA instructions per wave per stage
     static_assert(BLOCKS % NW == 0 && BM % RPB == 0, "DMA split");
     static_assert((STAGES - 2) * L < 64, "vmcnt range");
-    static_assert(STAGES >= 2 && STAGES <= (SCHED == SCHED_INTERLEAVE ? 5 : 4), "pipeline depth");
+    constexpr bool INTERLEAVED = SCHED != SCHED_PLAIN;
+    constexpr int PF_DIST = SCHED == SCHED_INTERLEAVE_PF ? 2 : 0;   // prefetch distance in k-tiles
+    static_assert(STAGES >= 2 && STAGES <= (INTERLEAVED ? 5 : 4), "pipeline depth");
     static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs in a wave");
 
-    __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS];
+    // the stages, then (prefetching schedule) 256 B per wave that the L2
+    // prefetch copies land in and nothing reads
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE_ELEMS + (PF_DIST > 0 ? NW * 128 : 0)];
 
     const int M = args.M, N = args.N, K = args.K;
     const int tiles_m = (M + BM - 1) / BM;
-    const int tiles_n = N / BN;
+    const int n_begin = args.n_begin;
+    const int tiles_n = ((args.n_end ? args.n_end : N) - n_begin) / BN;
     // Tile order: consecutive ids run on one XCD (xcd_remap); within the id
     // sequence, groups of up to 8 row panels are walked column by column, so the
     // ~32 tiles an XCD runs at once form an 8 x 4 block that shares A and W
@@ -78,17 +88,12 @@ gemm_bf16_kernel(GemmArgs args) {
     const int in_group = tile - group * (GM * tiles_n);
     const int m0 = (first_m + in_group % gm) * BM;
     const int tn = in_group / gm;
-    const int n0 = tn * BN;
+    const int n0 = n_begin + tn * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Main-loop schedules: SCHED_PLAIN (per k-tile: wait, barrier, copies,
-    // fragment reads and MFMAs, with latency hidden by the other waves of the
-    // SIMD) and SCHED_INTERLEAVE (one wave per SIMD, its LDS reads and copies
-    // threaded between its MFMAs).
-    static_assert(SCHED != SCHED_INTERLEAVE || (NW == 4 && (BK == 32 || BK == 64) && STAGES >= 2),
-                  "interleaved shape");
+    static_assert(!INTERLEAVED || (NW == 4 && (BK == 32 || BK == 64) && STAGES >= 2), "interleaved shape");
     const int wm = wave % WAVES_M;
     const int wn = wave / WAVES_M;
 
@@ -186,7 +191,7 @@ gemm_bf16_kernel(GemmArgs args) {
                 for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
     };
-    if constexpr (SCHED == SCHED_PLAIN) {
+    if constexpr (!INTERLEAVED) {
         // One k-tile: retire its copies (the STAGES-2 later ones stay in flight),
         // barrier, refill the stage that was read one step earlier, multiply.
         auto step = [&](int kt, int rd, int wr) {
@@ -249,6 +254,21 @@ gemm_bf16_kernel(GemmArgs args) {
             const int blk = wave + i * NW;
             dma16(src[i] + k_off(i, kt), lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
         };
+        // L2 prefetch (SCHED_INTERLEAVE_PF): each lane touches one 128-byte line
+        // of the k-tile PF_DIST ahead of the copies, in one of this wave's 64 A
+        // rows and 64 W rows, with a 4-byte LDS copy into the wave's scratch
+        // slot.  The copies of k-tile t+1 then mostly hit in L2.  The two
+        // prefetch loads are issued after the tile's copies, so waiting for the
+        // copies leaves them in flight (vector memory loads complete in order).
+        constexpr int NPF = PF_DIST > 0 ? 2 : 0;
+        const bf16_t* pf_a = A + (size_t)min(m0 + (wave * 64 + lane) % BM, M - 1) * K;
+        const int pf_n = n0 + (wave * 64 + lane) % BN;
+        const bf16_t* pf_w = W + (size_t)(pf_n >> 7) * (K / 64) * 8192 + (pf_n & 127) * 64;
+        const uint32_t pf_lds = lds_base + (uint32_t)(STAGES * STAGE_ELEMS * 2) + wave * 256;
+        auto prefetch = [&](int kt) {
+            dma4(pf_a + (size_t)kt * BK, pf_lds);
+            dma4(pf_w + (size_t)(BK == 64 ? kt : kt >> 1) * 8192, pf_lds);
+        };
         // the prologue issued k-tiles 0..STAGES-2 (clamped copies for small K
         // keep the count): k-tile 0 landed once (STAGES-2) L copies are pending
         for (int t = nk; t < STAGES - 1; ++t)
@@ -287,6 +307,7 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
                 for (int i = 0; i < L; ++i) dma_one(t_copy, st_copy, i);
             }
+            if constexpr (PF_DIST > 0) prefetch(min(t + PF_DIST, nk - 1));
             constexpr int LB = (KS - 1) & 1;  // fragment buffer of the last step
             // last step, first half
 #pragma unroll
@@ -294,8 +315,9 @@ gemm_bf16_kernel(GemmArgs args) {
                 mf(LB, n);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // k-tile t+1 landed (the copies of the STAGES-2 later ones stay in flight)
-            wait_vm_lgkm<(STAGES - 2) * L>();
+            // k-tile t+1 landed (the copies of the STAGES-2 later ones and this
+            // tile's prefetch loads stay in flight)
+            wait_vm_lgkm<(STAGES - 2) * L + NPF>();
             barrier();
             // last step, second half, with step 0's fragments of k-tile t+1
 #pragma unroll
@@ -401,7 +423,7 @@ gemm_bf16_kernel(GemmArgs args) {
                 float s = 0.f;
 #pragma unroll
                 for (int w = 0; w < WAVES_N; ++w) s += sPart[w * BM + rl];
-                e.ssq_out[(size_t)tn * M + m] = s;
+                e.ssq_out[(size_t)(n0 / BN) * M + m] = s;
             }
         }
     }
@@ -432,13 +454,11 @@ constexpr TileCfg kTiles[] = {
     {256, 128, 2, 2, 32, 3, 2, 0},  // 4 waves, wave tile 128x64, 72 KB: 2 workgroups per CU
     {128, 128, 2, 2, 32, 4, 2, 0},  // 4 waves, wave tile 64x64, 64 KB: 2 workgroups per CU
     {256, 256, 2, 2, 64, 2, 1, 1},  // 4 waves (1 per SIMD), wave tile 128x128, interleaved, BK 64
-    {256, 256, 2, 2, 32, 4, 1, 1},  // the same with BK 32 and 4 stages
+    {256, 256, 2, 2, 64, 2, 1, 2},  // the same with the L2 prefetch
     {256, 128, 2, 2, 64, 3, 1, 0},  // 4 waves, BK 64, 3 stages (144 KB)
-    {256, 192, 2, 2, 64, 2, 1, 1},  // interleaved, wave tile 128x96 (N = 6144: 256 tiles at M = 2048)
+    {256, 192, 2, 2, 64, 2, 1, 1},  // interleaved, wave tile 128x96
     {256, 128, 2, 2, 64, 3, 1, 1},  // interleaved, wave tile 128x64, 3 stages
-    {256, 256, 2, 2, 32, 5, 1, 1},  // interleaved 128x128, BK 32, 5 stages (160 KB)
-    {256, 192, 2, 2, 32, 5, 1, 1},  // interleaved 128x96, BK 32, 5 stages (140 KB)
-    {256, 128, 2, 2, 32, 5, 1, 1},  // interleaved 128x64, BK 32, 5 stages (120 KB)
+    {256, 256, 2, 2, 32, 4, 1, 1},  // interleaved 128x128, BK 32, 4 stages
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -452,7 +472,7 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
                   (EPI == EPI_RESID_NORM && WTN != 64 && WTN != 128)) {
         return hipErrorInvalidValue;
     } else {
-        const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
+        const int tiles = ((a.M + BM - 1) / BM) * (((a.n_end ? a.n_end : a.N) - a.n_begin) / BN);
         hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, ST, OCC, EPI, SCHED>), dim3(tiles),
                            dim3(64 * WM * WN), 0, s, a);
         return hipGetLastError();
@@ -501,18 +521,20 @@ void gemm_bf16_tile(int cfg, int* bm, int* bn, int* threads) {
 hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
     if (cfg < 0 || cfg >= kNumTiles) return hipErrorInvalidValue;
     if (a.M <= 0 || !gemm_bf16_supports(cfg, a.N, a.K, a.epi.kind)) return hipErrorInvalidValue;
+    const int n_end = a.n_end ? a.n_end : a.N;
+    const int bn = kTiles[cfg].bn;
+    if (a.n_begin < 0 || a.n_begin % bn != 0 || n_end % bn != 0 || n_end > a.N || a.n_begin >= n_end)
+        return hipErrorInvalidValue;
     switch (cfg) {
         case 0: return launch_cfg<256, 256, 4, 2, 64, 2, 2>(a, s);
         case 1: return launch_cfg<256, 128, 2, 2, 32, 3, 2>(a, s);
         case 2: return launch_cfg<128, 128, 2, 2, 32, 4, 2>(a, s);
         case 3: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_INTERLEAVE>(a, s);
-        case 4: return launch_cfg<256, 256, 2, 2, 32, 4, 1, SCHED_INTERLEAVE>(a, s);
+        case 4: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_INTERLEAVE_PF>(a, s);
         case 5: return launch_cfg<256, 128, 2, 2, 64, 3, 1>(a, s);
         case 6: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_INTERLEAVE>(a, s);
         case 7: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_INTERLEAVE>(a, s);
-        case 8: return launch_cfg<256, 256, 2, 2, 32, 5, 1, SCHED_INTERLEAVE>(a, s);
-        case 9: return launch_cfg<256, 192, 2, 2, 32, 5, 1, SCHED_INTERLEAVE>(a, s);
-        default: return launch_cfg<256, 128, 2, 2, 32, 5, 1, SCHED_INTERLEAVE>(a, s);
+        default: return launch_cfg<256, 256, 2, 2, 32, 4, 1, SCHED_INTERLEAVE>(a, s);
     }
 }
 

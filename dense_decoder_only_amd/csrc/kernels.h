@@ -52,6 +52,9 @@ struct GemmArgs {
     const float* ssq_in;
     int ssq_count;
     Epilogue epi;
+    // Output columns [n_begin, n_end) of this launch (prefill GEMM only; both
+    // multiples of the tile's BN; n_end = 0 means N).  N still sets the strides.
+    int n_begin, n_end;
 };
 
 // ---- bf16 MFMA projections -----------------------------------------------

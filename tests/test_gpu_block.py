@@ -86,6 +86,7 @@ BF16_SMALL = [
     (512, 8, 2, 768, 2, 2100, False),    # M = 4200: the 256x256 projection tiles, ragged M
     (256, 4, 2, 5120, 1, 1000, False),   # gate/up on the interleaved 4-wave kernel, ragged M, K = 256
     (2048, 16, 4, 512, 1, 3000, False),  # o and down on 256x128 BK-64 tiles, ragged M
+    (512, 8, 2, 5120, 1, 2048, False),   # gate/up: 1.25 rounds of 256x256 tiles, the tail on 256x128
 ]
 
 
