@@ -11,8 +11,9 @@ reports:
     FLOPs per launch over its average launch time, measured with HIP events on
     the launch stream over the timed region, against the bf16 MFMA peak;
   * cpu_baseline: the fp64 CPU oracle timed on the host on the same workload;
-  * other_workloads: 8B decode (B=32, P=1000), 70B decode (B=64, P=4096) and 70B
-    prefill (B=1, T=16384), each timed the same way (decode with two weight and
+  * other_workloads: 8B decode (B=32, P=1000), 70B decode (B=64, P=4096), 8B
+    chunked prefill (B=1, T=2048 at start 2048) and 70B prefill (B=1, T=16384),
+    each timed the same way (decode with two weight and
     cache sets used alternately so that the 256 MB last-level cache cannot hold
     the working set between steps), with per-stage times.
 Inputs are seeded synthetic tensors with the workload's shapes and
@@ -47,7 +48,7 @@ def stage_flops(wl):
     M = wl.B * wl.T
     d, hd, f = s.d_model, s.head_dim, s.d_ff
     if wl.mode == "prefill":
-        pairs = wl.B * wl.T * (wl.T + 1) // 2
+        pairs = wl.B * (wl.T * wl.P + wl.T * (wl.T + 1) // 2)
     else:
         pairs = wl.B * (wl.P + 1)
     return {
@@ -104,7 +105,9 @@ def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
     def step(i):
         blk = blocks[i % sets]
         kc, vc = caches[i % sets]
-        if wl.mode == "prefill":
+        if wl.mode == "prefill" and wl.P > 0:
+            llb.llb_block_prefill_at(blk, x, y, wl.B, wl.T, wl.P, kc, vc, cap, ws)
+        elif wl.mode == "prefill":
             llb.llb_block_prefill(blk, x, y, wl.B, wl.T, kc, vc, cap, ws)
         else:
             llb.llb_block_decode(blk, x, y, wl.B, wl.P, kc, vc, cap, ws)
@@ -286,8 +289,9 @@ def main():
 
     if not args.no_others and args.only is None:
         others = {}
-        for other, sets in (("8b_bf16_decode", 2), ("70b_bf16_decode", 2), ("70b_bf16_prefill", 1)):
-            steps = args.steps if "decode" in other else max(3, args.steps // 4)
+        for other, sets in (("8b_bf16_decode", 2), ("70b_bf16_decode", 2), ("8b_bf16_chunked_prefill", 1),
+                            ("70b_bf16_prefill", 1)):
+            steps = max(3, args.steps // 4) if other == "70b_bf16_prefill" else args.steps
             owl, oms, ost = time_workload(other, steps, max(2, args.warmup // 2), sets=sets)
             others[other] = summarize(owl, oms, ost)
             log(f"{other}: {oms:.3f} ms/step")

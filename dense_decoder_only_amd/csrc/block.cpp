@@ -568,6 +568,21 @@ llb_status llb_block_prefill(llb_block* b, const float* x, float* y, int32_t B, 
                      (hipStream_t)stream, false);
 }
 
+llb_status llb_block_prefill_at(llb_block* b, const float* x, float* y, int32_t B, int32_t T,
+                                int32_t start_pos, void* k_cache, void* v_cache, int32_t cache_cap,
+                                void* ws, size_t ws_bytes, void* stream) {
+    llb_status st = check_call(b, x, y, B, T, k_cache, v_cache, cache_cap, ws);
+    if (st != LLB_OK) return st;
+    if (start_pos < 0) return fail(LLB_E_INVALID, "start_pos must be >= 0");
+    if ((long)start_pos + T > cache_cap)
+        return fail(LLB_E_CAPACITY, "start_pos+T=%ld exceeds cache_cap=%d", (long)start_pos + T, cache_cap);
+    if ((long)start_pos + T > b->cfg.max_positions)
+        return fail(LLB_E_CAPACITY, "start_pos+T=%ld exceeds max_positions=%d", (long)start_pos + T,
+                    b->cfg.max_positions);
+    return run_block(b, x, y, B, T, start_pos, k_cache, v_cache, cache_cap, ws, ws_bytes,
+                     (hipStream_t)stream, false);
+}
+
 llb_status llb_block_decode(llb_block* b, const float* x, float* y, int32_t B, int32_t start_pos,
                             void* k_cache, void* v_cache, int32_t cache_cap, void* ws,
                             size_t ws_bytes, void* stream) {

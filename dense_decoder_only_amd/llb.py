@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "LLB_OK", -1: "LLB_E_INVALID", -2: "LLB_E_UNSUPPORTED", -3: "
                 -4: "LLB_E_HIP", -5: "LLB_E_NOMEM"}
 
 EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes",
-            "llb_block_prefill", "llb_block_decode", "llb_kv_append", "llb_attention_prefill",
+            "llb_block_prefill", "llb_block_prefill_at", "llb_block_decode", "llb_kv_append", "llb_attention_prefill",
             "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
             "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles",
             "llb_last_error")
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.llb_block_workspace_bytes.restype = sz
     lib.llb_block_prefill.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, vp, sz, vp]
     lib.llb_block_prefill.restype = ctypes.c_int
+    lib.llb_block_prefill_at.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, sz, vp]
+    lib.llb_block_prefill_at.restype = ctypes.c_int
     lib.llb_block_decode.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, vp, sz, vp]
     lib.llb_block_decode.restype = ctypes.c_int
     lib.llb_kv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
@@ -182,6 +184,12 @@ def llb_block_prefill(blk: Block, x, y, B, T, k_cache, v_cache, cache_cap, ws, s
     _check(load_library().llb_block_prefill(blk.handle, _ptr(x), _ptr(y), B, T, _ptr(k_cache),
                                             _ptr(v_cache), cache_cap, _ptr(ws), ws.numel() * ws.element_size(),
                                             _stream(stream)), "llb_block_prefill")
+
+
+def llb_block_prefill_at(blk: Block, x, y, B, T, start_pos, k_cache, v_cache, cache_cap, ws, stream=None):
+    _check(load_library().llb_block_prefill_at(blk.handle, _ptr(x), _ptr(y), B, T, start_pos, _ptr(k_cache),
+                                               _ptr(v_cache), cache_cap, _ptr(ws), ws.numel() * ws.element_size(),
+                                               _stream(stream)), "llb_block_prefill_at")
 
 
 def llb_block_decode(blk: Block, x, y, B, start_pos, k_cache, v_cache, cache_cap, ws, stream=None):

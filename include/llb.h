@@ -121,6 +121,19 @@ llb_status llb_block_prefill(llb_block* blk, const float* x, float* y, int32_t B
                              void* k_cache, void* v_cache, int32_t cache_cap,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Chunked prefill: T new tokens per sequence at positions
+ * start_pos..start_pos+T-1 against a cache whose rows 0..start_pos-1 already
+ * hold earlier tokens ("Llama 3 8B - Prepare Q, K, V": the model's forward
+ * takes the tokens and a start position and slices the rotation table from
+ * it).  Query t attends to cache rows 0..start_pos+t.  Writes the rotated keys
+ * and the values of the T tokens to cache rows start_pos..start_pos+T-1 and
+ * y = block(x).  x, y: [B, T, d_model] fp32 (y may alias x).  start_pos = 0 is
+ * llb_block_prefill.  Workspace: llb_block_workspace_bytes(blk, B, T).
+ * Needs start_pos >= 0 and start_pos + T <= cache_cap, <= max_positions. */
+llb_status llb_block_prefill_at(llb_block* blk, const float* x, float* y, int32_t B, int32_t T,
+                                int32_t start_pos, void* k_cache, void* v_cache,
+                                int32_t cache_cap, void* ws, size_t ws_bytes, void* stream);
+
 /* Decode: one new token per sequence at position start_pos = P, attending to
  * cache rows 0..P-1 plus its own key, L = P + 1 keys ("Llama 3 8B - Prepare Q,
  * K, V", header: decode reads L = P + 1 keys).  Writes cache row P and

@@ -78,6 +78,12 @@ class GpuBlock:
         llb.llb_block_prefill(self.blk, x, y, B, T, kc, vc, kc.shape[2], self.workspace(B, T))
         return y
 
+    def prefill_at(self, x, kc, vc, P):
+        B, T, _ = x.shape
+        y = torch.empty_like(x)
+        llb.llb_block_prefill_at(self.blk, x, y, B, T, P, kc, vc, kc.shape[2], self.workspace(B, T))
+        return y
+
     def decode(self, x, kc, vc, P):
         B = x.shape[0]
         y = torch.empty_like(x)

@@ -218,6 +218,100 @@ def test_bf16_prefill_then_decode_matches_longer_prefill():
     assert e <= 2e-2
 
 
+@pytest.mark.parametrize("B,P,T,G,scaled", [
+    (2, 300, 100, 4, False),    # chunk shorter than the prefix
+    (1, 37, 513, 4, False),     # several query tiles, key tiles straddle the prefix end
+    (1, 1000, 257, 8, True),    # group of 8, llama3-scaled RoPE at positions past 1000
+    (2, 500, 1100, 4, False),   # M = 2200: the 256x256 projection tiles, ragged
+])
+def test_bf16_chunked_prefill(B, P, T, G, scaled):
+    """T tokens at positions P..P+T-1 against a random cache prefix: y and the new
+    cache rows against the oracle; rows below P untouched, rows from P+T on keep
+    the sentinel."""
+    Hkv = 2
+    shp = shape(d_model=512, n_heads=G * Hkv, n_kv_heads=Hkv, head_dim=128, d_ff=768,
+                rope_scaling=scaled)
+    cap = workloads.cache_capacity(P + T)
+    w, x, kc, vc = gen_inputs(shp, 31 + P + T, B, T, P, cap, fill=SENTINEL)
+    note(f"chunked prefill bf16 B={B} P={P} T={T} G={G}")
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        kd, vd = kc.cuda(), vc.cuda()
+        y = gb.prefill_at(x.cuda(), kd, vd, P).cpu()
+        kd, vd = kd.cpu(), vd.cpu()
+    finally:
+        gb.close()
+    y_ref, k_ref, v_ref = oracle.block_forward(shp, w, x, kc, vc, P)
+    e_y = rel_err(y, y_ref)
+    e_k = bf16_err(kd[:, :, P:P + T], k_ref)
+    e_v = bf16_err(vd[:, :, P:P + T], v_ref)
+    note(f"  y {e_y:.2e}  k {e_k:.3f}  v {e_v:.3f}")
+    assert e_y <= 2e-2 and e_k <= 1.0 and e_v <= 1.0
+    assert torch.equal(kd[:, :, :P], kc[:, :, :P]) and torch.equal(vd[:, :, :P], vc[:, :, :P])
+    assert torch.all(kd[:, :, P + T:].float() == SENTINEL)
+
+
+def test_f32_chunked_prefill():
+    wl = workloads.get("tiny_f32_prefill")
+    shp = wl.shape
+    B, P, T = 2, 40, 24
+    cap = workloads.cache_capacity(P + T)
+    w, x, kc, vc = gen_inputs(shp, 77, B, T, P, cap, fill=SENTINEL)
+    note(f"chunked prefill f32 B={B} P={P} T={T}")
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        kd, vd = kc.cuda(), vc.cuda()
+        y = gb.prefill_at(x.cuda(), kd, vd, P).cpu()
+        kd, vd = kd.cpu(), vd.cpu()
+    finally:
+        gb.close()
+    y_ref, k_ref, v_ref = oracle.block_forward(shp, w, x, kc, vc, P)
+    e_y, e_k, e_v = rel_err(y, y_ref), rel_err(kd[:, :, P:P + T], k_ref), rel_err(vd[:, :, P:P + T], v_ref)
+    note(f"  y {e_y:.2e}  k {e_k:.2e}  v {e_v:.2e}")
+    assert e_y <= 1e-5 and e_k <= 1e-5 and e_v <= 1e-5
+    assert torch.equal(kd[:, :, :P], kc[:, :, :P])
+    assert torch.all(kd[:, :, P + T:] == SENTINEL)
+
+
+def test_bf16_prefill_in_chunks_matches_one_prefill():
+    """GPU prefill of the first T1 tokens, then a GPU chunk of T2 at start T1: the
+    chunk's outputs equal rows T1.. of the oracle's single prefill of T1 + T2."""
+    shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+    B, T1, T2 = 2, 300, 200
+    cap = workloads.cache_capacity(T1 + T2)
+    w, x, kc, vc = gen_inputs(shp, 41, B, T1 + T2, 0, cap, fill=SENTINEL)
+    note("prefill -> chunked prefill continuation")
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        kd, vd, xd = kc.cuda(), vc.cuda(), x.cuda()
+        gb.prefill(xd[:, :T1].contiguous(), kd, vd)
+        y = gb.prefill_at(xd[:, T1:].contiguous(), kd, vd, T1).cpu()
+    finally:
+        gb.close()
+    y_ref, _, _ = oracle.block_forward(shp, w, x, kc, vc, 0, rows=list(range(T1, T1 + T2)))
+    e = rel_err(y, y_ref)
+    note(f"  y {e:.2e}")
+    assert e <= 2e-2
+
+
+def test_chunked_prefill_rejects_bad_positions():
+    from dense_decoder_only_amd import llb
+    shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+    cap = 64
+    w, x, kc, vc = gen_inputs(shp, 3, 1, 16, 0, cap)
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        kd, vd, xd = kc.cuda(), vc.cuda(), x.cuda()
+        for P, status in ((-1, llb.LLB_E_INVALID), (cap - 15, llb.LLB_E_CAPACITY)):
+            with pytest.raises(llb.LlbError) as ei:
+                gb.prefill_at(xd, kd, vd, P)
+            assert ei.value.status == status
+        torch.cuda.synchronize()
+        assert torch.equal(kd.cpu(), kc)                      # nothing was written
+    finally:
+        gb.close()
+
+
 def test_bf16_prefill_is_deterministic():
     shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
     B, T = 2, 130

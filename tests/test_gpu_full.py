@@ -1,7 +1,8 @@
 """Block parity at the full workload sizes, in the launch configuration that
 bench.py times (same entry points, shapes and dtypes).
 
-  * 8B prefill (B=1, T=2048) and 8B decode (B=32, P=1000): every output row.
+  * 8B prefill (B=1, T=2048), 8B chunked prefill (B=1, T=2048 at start 2048) and
+    8B decode (B=32, P=1000): every output row.
   * 70B decode (B=64, P=4096, llama3-scaled RoPE): every output row.
   * 70B long prefill (B=1, T=16384): keys/values for all 16384 tokens are checked
     against the oracle; y on a fixed set of sampled rows (first, last, tile edges),
@@ -29,7 +30,7 @@ def _inputs(wl):
     return workloads.make_inputs(wl, cap=cap)
 
 
-@pytest.mark.parametrize("name", ["8b_bf16_prefill", "70b_bf16_prefill"])
+@pytest.mark.parametrize("name", ["8b_bf16_prefill", "70b_bf16_prefill", "8b_bf16_chunked_prefill"])
 def test_full_prefill(name):
     wl = workloads.get(name)
     note(f"full {name}: generating inputs")
@@ -38,8 +39,8 @@ def test_full_prefill(name):
     gb = GpuBlock(wl.shape, inp["weights"], max_positions=cap)
     try:
         kd, vd = inp["k_cache"].cuda(), inp["v_cache"].cuda()
-        note(f"full {name}: GPU prefill B={wl.B} T={wl.T}")
-        y = gb.prefill(inp["x"].cuda(), kd, vd)
+        note(f"full {name}: GPU prefill B={wl.B} T={wl.T} at start {wl.P}")
+        y = gb.prefill_at(inp["x"].cuda(), kd, vd, wl.P) if wl.P else gb.prefill(inp["x"].cuda(), kd, vd)
         torch.cuda.synchronize()
         y, kd, vd = y.cpu(), kd.cpu(), vd.cpu()
     finally:
@@ -47,12 +48,13 @@ def test_full_prefill(name):
     rows = C5_ROWS if wl.T > 4096 else None
     note(f"full {name}: oracle (rows={'sampled' if rows else 'all'})")
     y_ref, k_ref, v_ref = oracle.block_forward(wl.shape, inp["weights"], inp["x"], inp["k_cache"],
-                                               inp["v_cache"], 0, rows=rows)
+                                               inp["v_cache"], wl.P, rows=rows)
     if rows is not None:
         y = y[:, rows]
     e_y = rel_err(y, y_ref)
-    e_k = bf16_err(kd[:, :, :wl.T], k_ref)
-    e_v = bf16_err(vd[:, :, :wl.T], v_ref)
+    e_k = bf16_err(kd[:, :, wl.P:wl.P + wl.T], k_ref)
+    e_v = bf16_err(vd[:, :, wl.P:wl.P + wl.T], v_ref)
+    assert torch.equal(kd[:, :, :wl.P], inp["k_cache"][:, :, :wl.P])
     note(f"full {name}: y {e_y:.3e} k {e_k:.3f} v {e_v:.3f}")
     assert e_y <= 2e-2
     assert e_k <= 1.0 and e_v <= 1.0

@@ -89,7 +89,7 @@ class Workload:
     mode: str          # "prefill" or "decode"
     B: int
     T: int = 1         # new tokens per sequence (1 for decode)
-    P: int = 0         # cached positions before the call (decode start position)
+    P: int = 0         # cached positions before the call (start position)
     seed: int = 0
 
     @property
@@ -108,6 +108,10 @@ CONFIGS: Dict[str, Workload] = {
     "8b_bf16_decode": Workload("8b_bf16_decode", LLAMA31_8B, "decode", B=32, T=1, P=1000, seed=3),
     "70b_bf16_decode": Workload("70b_bf16_decode", LLAMA31_70B, "decode", B=64, T=1, P=4096, seed=4),
     "70b_bf16_prefill": Workload("70b_bf16_prefill", LLAMA31_70B, "prefill", B=1, T=16384, seed=5),
+    # second 2048-token chunk of a 4096-token prompt: positions 2048..4095 over a
+    # 2048-row cache prefix
+    "8b_bf16_chunked_prefill": Workload("8b_bf16_chunked_prefill", LLAMA31_8B, "prefill", B=1, T=2048,
+                                        P=2048, seed=6),
 }
 
 
