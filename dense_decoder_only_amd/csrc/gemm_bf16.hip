@@ -139,26 +139,35 @@ gemm_bf16_kernel(GemmArgs args) {
         }
     };
 
-    // Row scale of the normalised-operand epilogues, loaded before the first
-    // copies are issued (waiting for these loads does not drain the pipeline)
-    // and parked in LDS after the main loop.  Every row of the tile has one
-    // thread (BM <= threads).
     static_assert(BM <= 64 * NW, "one thread per tile row");
     constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
-    float row_scale = 1.0f;
-    if constexpr (SCALED) {
-        const int m = m0 + tid;
-        if (tid < BM && m < M) {
-            float s = 0.f;
-            for (int p = 0; p < args.ssq_count; ++p) s += args.ssq_in[(size_t)p * M + m];
-            row_scale = inv_rms(s, K, args.eps);
-        }
-    }
-
     const int nk = K / BK;
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
         if (st < nk) issue(st, st);
+
+    // Row scale of the normalised-operand epilogues (one thread per tile row),
+    // loaded after the first copies so that its loads wait alongside theirs;
+    // the partial sums of squares are fetched eight at a time and added in
+    // index order.  Parked in LDS after the main loop.
+    float row_scale = 1.0f;
+    if constexpr (SCALED) {
+        const int m = m0 + tid;
+        if (tid < BM && m < M) {
+            const float* ssq = args.ssq_in + m;
+            float s = 0.f;
+            int p = 0;
+            for (; p + 8 <= args.ssq_count; p += 8) {
+                float v[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = ssq[(size_t)(p + q) * M];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) s += v[q];
+            }
+            for (; p < args.ssq_count; ++p) s += ssq[(size_t)p * M];
+            row_scale = inv_rms(s, K, args.eps);
+        }
+    }
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -357,10 +366,18 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int rbase = wm * WTM + i * 32 + half * HR;   // tile row of the staged rows
+            // staged row rr of register r: 8 (r / 4) + 4 (lane / 32) + r % 4 - 16 half,
+            // i.e. two runs of 4 consecutive rows whose scales are read at once
+            float4 sc4[2] = {make_float4(1.f, 1.f, 1.f, 1.f), make_float4(1.f, 1.f, 1.f, 1.f)};
+            if constexpr (SCALED) {
+                sc4[0] = *(const float4*)&sScale[rbase + 4 * (lane >> 5)];
+                sc4[1] = *(const float4*)&sScale[rbase + 8 + 4 * (lane >> 5)];
+            }
 #pragma unroll
             for (int r = 8 * half; r < 8 * half + 8; ++r) {
                 const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - half * HR;
-                const float sc = SCALED ? sScale[rbase + rr] : 1.0f;
+                const float4 s4 = sc4[(r >> 2) & 1];
+                const float sc = (r & 3) == 0 ? s4.x : (r & 3) == 1 ? s4.y : (r & 3) == 2 ? s4.z : s4.w;
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     stile[rr * SROW + j * 32 + (lane & 31)] = acc[i][j][r] * sc;
