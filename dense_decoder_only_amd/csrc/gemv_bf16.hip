@@ -286,13 +286,12 @@ size_t partial_bytes(int M, int N, int splits) {
 }  // namespace
 
 // Split count, from measurements on MI355X: the fewest splits that give at
-// least 128 workgroups (M <= 32) or 192 (M <= 64, whose stages are larger);
-// more splits only add partial traffic and reduction work.  Every split keeps
-// at least 4 k-tiles of 64.
+// least 192 workgroups; more splits only add partial traffic and reduction
+// work.  Every split keeps at least 4 k-tiles of 64.
 int gemv_bf16_splits(int M, int N, int K) {
     const int tiles = N / GV_BN;
     const int nkt = K / GV_BK;
-    const int target = M <= 32 ? 128 : 192;
+    const int target = 192;
     int s = (target + tiles - 1) / tiles;
     s = std::max(1, std::min(s, nkt / 4));
     return s;
