@@ -212,27 +212,32 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 }
 
 // Picks the prefill tile configuration (see gemm_bf16.hip) of C[M,N] = A[M,K] W^T
-// from measurements of the whole block on MI355X (steady clocks):
-//  - long inputs (M >= 4096): 256x256 tiles; the interleaved 4-wave kernel
-//    with the L2 prefetch for long K or wide N, the 8-wave kernel otherwise;
+// with epilogue kind epi, from measurements of the whole block on MI355X
+// (steady clocks):
+//  - long inputs (M >= 4096): 256x256 tiles; for the normalised-operand
+//    projections (QKV, gate/up) the interleaved kernel on 16x16x32 MFMAs with
+//    the L2 prefetch, for the others the interleaved 32x32x16 kernel with the
+//    prefetch at long K and the 8-wave kernel otherwise;
 //  - 256x192 tiles when they fill whole rounds of the 256 compute units;
-//  - 256x256 tiles (8-wave kernel) once they fill at least 160 compute units;
+//  - 256x256 tiles once they fill at least 160 compute units (gate/up on the
+//    16x16x32 prefetching kernel, the rest on the 8-wave kernel);
 //  - 256x128 tiles (interleaved, BK 64, 3 stages) from 192 tiles up when K is
 //    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that.
-int pick_tile(int M, int N, int K) {
+int pick_tile(int M, int N, int K, int epi) {
     const int pm = (M + 255) / 256;
-    if (N % 256 == 0 && M >= 4096) return (K >= 16384 || N >= 32768) ? 4 : 0;
+    const bool scaled = epi == llb::EPI_QKV || epi == llb::EPI_SWIGLU;
+    if (N % 256 == 0 && M >= 4096) return scaled ? 10 : (K >= 16384 || N >= 32768) ? 4 : 0;
     if (N % 128 != 0) return -1;
     if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return 6;
-    if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return 0;
+    if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 10 : 0;
     const long t128 = (long)pm * (N / 128);
     if (t128 >= 192 && K % 64 == 0) return 7;
     return M > 128 ? 1 : 2;
 }
 
-int tile_for(const llb_block* b, int override_cfg, int M, int N, int K) {
+int tile_for(const llb_block* b, int override_cfg, int M, int N, int K, int epi) {
     (void)b;
-    return override_cfg >= 0 ? override_cfg : pick_tile(M, N, K);
+    return override_cfg >= 0 ? override_cfg : pick_tile(M, N, K, epi);
 }
 
 // The 256x128 interleaved configuration that takes over a projection's last,
@@ -311,10 +316,10 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     const bool bf16 = c.wdtype == LLB_BF16;
     const bool small_m = decode && M <= 64;
     const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * hd;
-    const int tile_qkv = tile_for(b, b->tile_qkv, M, nqkv, d);
-    const int tile_o = tile_for(b, b->tile_o, M, d, c.n_heads * hd);
-    const int tile_gu = tile_for(b, b->tile_gu, M, 2 * c.d_ff, d);
-    const int tile_down = tile_for(b, b->tile_down, M, d, c.d_ff);
+    const int tile_qkv = tile_for(b, b->tile_qkv, M, nqkv, d, llb::EPI_QKV);
+    const int tile_o = tile_for(b, b->tile_o, M, d, c.n_heads * hd, llb::EPI_RESID_NORM);
+    const int tile_gu = tile_for(b, b->tile_gu, M, 2 * c.d_ff, d, llb::EPI_SWIGLU);
+    const int tile_down = tile_for(b, b->tile_down, M, d, c.d_ff, llb::EPI_RESID);
     if (bf16 && !small_m) {
         // every projection's tile fits before anything is queued
         const struct { int cfg, N, K, epi; const char* what; } chk[] = {

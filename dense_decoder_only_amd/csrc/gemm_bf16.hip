@@ -45,8 +45,12 @@ LLB_DEV int swz(int r) {
 // fragment reads and MFMAs, with latency hidden by the other waves of the
 // SIMD), SCHED_INTERLEAVE (one wave per SIMD, its LDS reads and copies
 // threaded between its MFMAs) and SCHED_INTERLEAVE_PF (the same, plus an L2
-// prefetch of the operand lines two k-tiles ahead of the copies).
-constexpr int SCHED_PLAIN = 0, SCHED_INTERLEAVE = 1, SCHED_INTERLEAVE_PF = 2;
+// prefetch of the operand lines two k-tiles ahead of the copies), all on
+// 32x32x16 MFMAs; SCHED_I16 and SCHED_I16_PF are the interleaved schedules on
+// 16x16x32 MFMAs, which do the same work at a lower power draw (more clock
+// under the chip's power limit, measured on random operands).
+constexpr int SCHED_PLAIN = 0, SCHED_INTERLEAVE = 1, SCHED_INTERLEAVE_PF = 2, SCHED_I16 = 3,
+              SCHED_I16_PF = 4;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OCC, int EPI, int SCHED>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(OCC)))
@@ -64,7 +68,12 @@ gemm_bf16_kernel(GemmArgs args) {
     static_assert(BLOCKS % NW == 0 && BM % RPB == 0, "DMA split");
     static_assert((STAGES - 2) * L < 64, "vmcnt range");
     constexpr bool INTERLEAVED = SCHED != SCHED_PLAIN;
-    constexpr int PF_DIST = SCHED == SCHED_INTERLEAVE_PF ? 2 : 0;   // prefetch distance in k-tiles
+    constexpr bool M16 = SCHED == SCHED_I16 || SCHED == SCHED_I16_PF;   // 16x16x32 MFMAs
+    constexpr int PF_DIST = (SCHED == SCHED_INTERLEAVE_PF || SCHED == SCHED_I16_PF) ? 2 : 0;  // in k-tiles
+    constexpr int MB = M16 ? 16 : 32;          // MFMA block edge
+    constexpr int KSTEP = M16 ? 32 : 16;       // k per MFMA
+    constexpr int TMB = WTM / MB, TNB = WTN / MB;
+    static_assert(WTM % MB == 0 && WTN % MB == 0 && BK % KSTEP == 0, "MFMA blocks");
     static_assert(STAGES >= 2 && STAGES <= (INTERLEAVED ? 5 : 4), "pipeline depth");
     static_assert(EPI != EPI_SWIGLU || (WTN % 64) == 0, "SwiGLU needs gate/up pairs in a wave");
 
@@ -169,13 +178,22 @@ gemm_bf16_kernel(GemmArgs args) {
         }
     }
 
-    f32x16 acc[TM][TN];
+    // accumulators: 32x32 blocks (acc) or 16x16 blocks (acc16); the other is unused
+    f32x16 acc[M16 ? 1 : TM][M16 ? 1 : TN];
+    f32x4 acc16[M16 ? TMB : 1][M16 ? TNB : 1];
+    if constexpr (M16) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TMB; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TNB; ++j) acc16[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
 
     auto compute = [&](int st) {
         const bf16_t* a_s = smem + st * STAGE_ELEMS;
@@ -219,45 +237,49 @@ gemm_bf16_kernel(GemmArgs args) {
                 if (kt + st < nk) step(kt + st, st, (st + STAGES - 1) % STAGES);
         }
     } else {
-        // Interleaved: one wave per SIMD owns a WTM x WTN block (TM x TN MFMA
-        // blocks, NM = TM*TN MFMAs per k-step of 16, NR = TM+TN fragment
-        // reads).  Within k-tile t, the MFMAs of steps 0..KS-2 are threaded with
+        // Interleaved: one wave per SIMD owns a WTM x WTN block (TMB x TNB MFMA
+        // blocks of MB x MB, NM = TMB*TNB MFMAs per k-step of KSTEP, NR =
+        // TMB+TNB fragment reads).  Within k-tile t, the MFMAs of steps 0..KS-2 are threaded with
         // the reads of the next step's fragments (first) and this k-tile's share
         // of the copies of k-tile t+STAGES-1 into the stage of k-tile t-1; the
         // MFMAs of the last step are split around the wait + barrier that
         // publishes k-tile t+1, after which step 0's fragments of k-tile t+1 are
         // read between the remaining MFMAs.  Every element is pinned in place
         // with a scheduling barrier.
-        constexpr int NM = TM * TN, NR = TM + TN;
-        constexpr int KS = BK / 16;
+        constexpr int NM = TMB * TNB, NR = TMB + TNB;
+        constexpr int KS = BK / KSTEP;
         static_assert(NR <= NM, "reads ride on the MFMAs");
-        bf16x8 fa[2][TM], fb[2][TN];
+        bf16x8 fa[2][TMB], fb[2][TNB];
         uint32_t a_off[KS], b_off[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            const int c = 2 * kk + (lane >> 5);
-            const int ra = wm * WTM + (lane & 31), rb = wn * WTN + (lane & 31);
+            // fragment of an MB-row block: lane -> row lane % MB, 16-byte k-chunk
+            // (KSTEP / 8) kk + lane / MB
+            const int c = (KSTEP / 8) * kk + lane / MB;
+            const int ra = wm * WTM + lane % MB, rb = wn * WTN + lane % MB;
             a_off[kk] = lds_base + (uint32_t)((ra * BK + ((c ^ swz<BK>(ra)) << 3)) * 2);
             b_off[kk] = lds_base + (uint32_t)((BM * BK + rb * BK + ((c ^ swz<BK>(rb)) << 3)) * 2);
         }
         constexpr uint32_t STAGE_BYTES = STAGE_ELEMS * 2;
         typedef bf16x8 __attribute__((address_space(3))) * lds_frag_ptr;
+        // (the swizzle of row r + MB i equals that of r: MB i / 2 is a multiple of 8)
         auto rd_a = [&](int st, int kk, int fbuf, int i) {
-            fa[fbuf][i] = *(lds_frag_ptr)(uintptr_t)(a_off[kk] + st * STAGE_BYTES + i * 32 * BK * 2);
+            fa[fbuf][i] = *(lds_frag_ptr)(uintptr_t)(a_off[kk] + st * STAGE_BYTES + i * MB * BK * 2);
         };
         auto rd_b = [&](int st, int kk, int fbuf, int j) {
-            fb[fbuf][j] = *(lds_frag_ptr)(uintptr_t)(b_off[kk] + st * STAGE_BYTES + j * 32 * BK * 2);
+            fb[fbuf][j] = *(lds_frag_ptr)(uintptr_t)(b_off[kk] + st * STAGE_BYTES + j * MB * BK * 2);
         };
         // n-th of the NR fragment reads, in the order the MFMAs (i-major) first
-        // use them: A0 B0 .. B(TN-1) A1 .. A(TM-1)
+        // use them: A0 B0 .. B(TNB-1) A1 .. A(TMB-1)
         auto rd = [&](int st, int kk, int fbuf, int n) {
             if (n == 0) rd_a(st, kk, fbuf, 0);
-            else if (n <= TN) rd_b(st, kk, fbuf, n - 1);
-            else rd_a(st, kk, fbuf, n - TN);
+            else if (n <= TNB) rd_b(st, kk, fbuf, n - 1);
+            else rd_a(st, kk, fbuf, n - TNB);
         };
         auto mf = [&](int fbuf, int n) {  // n-th of the NM MFMAs of a k-step
-            const int i = n / TN, j = n % TN;
-            acc[i][j] = mfma32(fa[fbuf][i], fb[fbuf][j], acc[i][j]);
+            const int i = n / TNB, j = n % TNB;
+            if constexpr (M16) acc16[i][j] = mfma16(fa[fbuf][i], fb[fbuf][j], acc16[i][j]);
+            else acc[i][j] = mfma32(fa[fbuf][i], fb[fbuf][j], acc[i][j]);
         };
         auto dma_one = [&](int kt, int st, int i) {
             const int blk = wave + i * NW;
@@ -361,74 +383,99 @@ gemm_bf16_kernel(GemmArgs args) {
         if (tid < BM) sScale[tid] = row_scale;
         __syncthreads();
     }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int rbase = wm * WTM + i * 32 + half * HR;   // tile row of the staged rows
-            // staged row rr of register r: 8 (r / 4) + 4 (lane / 32) + r % 4 - 16 half,
-            // i.e. two runs of 4 consecutive rows whose scales are read at once
-            float4 sc4[2] = {make_float4(1.f, 1.f, 1.f, 1.f), make_float4(1.f, 1.f, 1.f, 1.f)};
-            if constexpr (SCALED) {
-                sc4[0] = *(const float4*)&sScale[rbase + 4 * (lane >> 5)];
-                sc4[1] = *(const float4*)&sScale[rbase + 8 + 4 * (lane >> 5)];
+    // the staged rows rbase .. rbase + HR - 1 of this wave's slice, from LDS to
+    // the epilogue
+    auto flush = [&](int rbase) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if constexpr (EPI == EPI_SWIGLU) {
+            constexpr int CPR = WTN / 16;         // (gate, up) chunk pairs per row
+            for (int idx = lane; idx < HR * CPR; idx += 64) {
+                const int row = idx / CPR, ch = idx % CPR;
+                const int cg = (ch >> 2) * 64 + (ch & 3) * 8;   // gate columns in the slice
+                const int m = m0 + rbase + row;
+                float g[8], u[8];
+                *(float4*)&g[0] = *(const float4*)&stile[row * SROW + cg];
+                *(float4*)&g[4] = *(const float4*)&stile[row * SROW + cg + 4];
+                *(float4*)&u[0] = *(const float4*)&stile[row * SROW + cg + 32];
+                *(float4*)&u[4] = *(const float4*)&stile[row * SROW + cg + 36];
+                const int f = ((n0 + wn * WTN + cg - (cg & 63)) >> 1) + (cg & 63);
+                if (m < M) epi_swiglu8(e, m, f, N >> 1, g, u);
             }
+        } else {
+            constexpr int CPR = WTN / 8;          // 8-column chunks per row
+            for (int idx = lane; idx < HR * CPR; idx += 64) {
+                const int row = idx / CPR, ch = idx % CPR;
+                const int m = m0 + rbase + row;
+                const int n = n0 + wn * WTN + ch * 8;
+                float v[8];
+                *(float4*)&v[0] = *(const float4*)&stile[row * SROW + ch * 8];
+                *(float4*)&v[4] = *(const float4*)&stile[row * SROW + ch * 8 + 4];
+                if constexpr (EPI == EPI_QKV) {
+                    if (m < M) epi_qkv8(e, m, n, v);
+                } else {
+                    float ss = 0.f;
+                    if (m < M) {
+                        epi_resid8(e, m, n, N, v);
+                        if constexpr (EPI == EPI_RESID_NORM) ss = epi_norm_operand8(e, m, n, N, v);
+                    }
+                    if constexpr (EPI == EPI_RESID_NORM) {
+                        // the CPR lanes of one row are consecutive: reduce over them
+                        static_assert(CPR == 16 || CPR == 8, "row reduction width");
 #pragma unroll
-            for (int r = 8 * half; r < 8 * half + 8; ++r) {
-                const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - half * HR;
-                const float4 s4 = sc4[(r >> 2) & 1];
-                const float sc = (r & 3) == 0 ? s4.x : (r & 3) == 1 ? s4.y : (r & 3) == 2 ? s4.z : s4.w;
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    stile[rr * SROW + j * 32 + (lane & 31)] = acc[i][j][r] * sc;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if constexpr (EPI == EPI_SWIGLU) {
-                constexpr int CPR = WTN / 16;         // (gate, up) chunk pairs per row
-                for (int idx = lane; idx < HR * CPR; idx += 64) {
-                    const int row = idx / CPR, ch = idx % CPR;
-                    const int cg = (ch >> 2) * 64 + (ch & 3) * 8;   // gate columns in the slice
-                    const int m = m0 + rbase + row;
-                    float g[8], u[8];
-                    *(float4*)&g[0] = *(const float4*)&stile[row * SROW + cg];
-                    *(float4*)&g[4] = *(const float4*)&stile[row * SROW + cg + 4];
-                    *(float4*)&u[0] = *(const float4*)&stile[row * SROW + cg + 32];
-                    *(float4*)&u[4] = *(const float4*)&stile[row * SROW + cg + 36];
-                    const int f = ((n0 + wn * WTN + cg - (cg & 63)) >> 1) + (cg & 63);
-                    if (m < M) epi_swiglu8(e, m, f, N >> 1, g, u);
-                }
-            } else {
-                constexpr int CPR = WTN / 8;          // 8-column chunks per row
-                for (int idx = lane; idx < HR * CPR; idx += 64) {
-                    const int row = idx / CPR, ch = idx % CPR;
-                    const int m = m0 + rbase + row;
-                    const int n = n0 + wn * WTN + ch * 8;
-                    float v[8];
-                    *(float4*)&v[0] = *(const float4*)&stile[row * SROW + ch * 8];
-                    *(float4*)&v[4] = *(const float4*)&stile[row * SROW + ch * 8 + 4];
-                    if constexpr (EPI == EPI_QKV) {
-                        if (m < M) epi_qkv8(e, m, n, v);
-                    } else {
-                        float ss = 0.f;
-                        if (m < M) {
-                            epi_resid8(e, m, n, N, v);
-                            if constexpr (EPI == EPI_RESID_NORM) ss = epi_norm_operand8(e, m, n, N, v);
-                        }
-                        if constexpr (EPI == EPI_RESID_NORM) {
-                            // the CPR lanes of one row are consecutive: reduce over them
-                            static_assert(CPR == 16 || CPR == 8, "row reduction width");
-#pragma unroll
-                            for (int off = 1; off < CPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
-                            if ((lane % CPR) == 0) sPart[wn * BM + rbase + row] = ss;
-                        }
+                        for (int off = 1; off < CPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                        if ((lane % CPR) == 0) sPart[wn * BM + rbase + row] = ss;
                     }
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    if constexpr (M16) {
+        // 16x16 blocks: register r of block (i, j) is row 16 i + 4 (lane / 16) + r,
+        // column 16 j + lane % 16; a block row of 16 is one staging pass
+        static_assert(HR == 16, "one 16-row block per pass");
+#pragma unroll
+        for (int i = 0; i < TMB; ++i) {
+            const int rbase = wm * WTM + i * 16;
+            float4 sc4 = make_float4(1.f, 1.f, 1.f, 1.f);
+            if constexpr (SCALED) sc4 = *(const float4*)&sScale[rbase + 4 * (lane >> 4)];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rr = 4 * (lane >> 4) + r;
+                const float sc = r == 0 ? sc4.x : r == 1 ? sc4.y : r == 2 ? sc4.z : sc4.w;
+#pragma unroll
+                for (int j = 0; j < TNB; ++j) stile[rr * SROW + j * 16 + (lane & 15)] = acc16[i][j][r] * sc;
+            }
+            flush(rbase);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int rbase = wm * WTM + i * 32 + half * HR;   // tile row of the staged rows
+                // staged row rr of register r: 8 (r / 4) + 4 (lane / 32) + r % 4 - 16 half,
+                // i.e. two runs of 4 consecutive rows whose scales are read at once
+                float4 sc4[2] = {make_float4(1.f, 1.f, 1.f, 1.f), make_float4(1.f, 1.f, 1.f, 1.f)};
+                if constexpr (SCALED) {
+                    sc4[0] = *(const float4*)&sScale[rbase + 4 * (lane >> 5)];
+                    sc4[1] = *(const float4*)&sScale[rbase + 8 + 4 * (lane >> 5)];
+                }
+#pragma unroll
+                for (int r = 8 * half; r < 8 * half + 8; ++r) {
+                    const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) - half * HR;
+                    const float4 s4 = sc4[(r >> 2) & 1];
+                    const float sc = (r & 3) == 0 ? s4.x : (r & 3) == 1 ? s4.y : (r & 3) == 2 ? s4.z : s4.w;
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        stile[rr * SROW + j * 32 + (lane & 31)] = acc[i][j][r] * sc;
+                }
+                flush(rbase);
+            }
         }
     }
 
@@ -476,6 +523,10 @@ constexpr TileCfg kTiles[] = {
     {256, 192, 2, 2, 64, 2, 1, 1},  // interleaved, wave tile 128x96
     {256, 128, 2, 2, 64, 3, 1, 1},  // interleaved, wave tile 128x64, 3 stages
     {256, 256, 2, 2, 32, 4, 1, 1},  // interleaved 128x128, BK 32, 4 stages
+    {256, 256, 2, 2, 64, 2, 1, 3},  // 3 on 16x16x32 MFMAs
+    {256, 256, 2, 2, 64, 2, 1, 4},  // 4 on 16x16x32 MFMAs
+    {256, 128, 2, 2, 64, 3, 1, 3},  // 7 on 16x16x32 MFMAs
+    {256, 192, 2, 2, 64, 2, 1, 3},  // 6 on 16x16x32 MFMAs
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -551,7 +602,11 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
         case 5: return launch_cfg<256, 128, 2, 2, 64, 3, 1>(a, s);
         case 6: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_INTERLEAVE>(a, s);
         case 7: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_INTERLEAVE>(a, s);
-        default: return launch_cfg<256, 256, 2, 2, 32, 4, 1, SCHED_INTERLEAVE>(a, s);
+        case 8: return launch_cfg<256, 256, 2, 2, 32, 4, 1, SCHED_INTERLEAVE>(a, s);
+        case 9: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_I16>(a, s);
+        case 10: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
+        case 11: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_I16>(a, s);
+        default: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16>(a, s);
     }
 }
 
