@@ -1,6 +1,6 @@
 """Benchmark of the Llama-3 block library on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-others]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-seconds S] [--no-cpu-baseline] [--no-others]
 
 One step is one llb_block_prefill call of the Llama-3.1-8B block on B=1 x
 T=2048 tokens (RMSNorm+QKV+RoPE+cache write, causal GQA attention, O projection
@@ -219,6 +219,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="keep warming up until this much time has passed (clocks settle under load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--only", default=None, help="time only this workload (diagnostics)")
@@ -246,7 +248,7 @@ def main():
         return
 
     name = args.only or HEADLINE
-    wl, ms, st = time_workload(name, args.steps, args.warmup)
+    wl, ms, st = time_workload(name, args.steps, args.warmup, warm_seconds=args.warmup_seconds)
     head = summarize(wl, ms, st)
     log(f"{name}: {ms:.3f} ms/step, {head['tokens_per_s']:.0f} tok/s")
 
@@ -254,10 +256,17 @@ def main():
     dom = "gate_up"
     if wl.mode == "prefill":
         achieved = fl[dom] / (st[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "gemm_bf16_kernel (gate/up projection, RMSNorm + SiLU.up fused)",
+        # The gate/up projection is one or two back-to-back launches of
+        # gemm_bf16_kernel: on the 8B shape, 3 rounds of 256x256 tiles, then the
+        # last, partly filled round as 256x128 tiles.  The HIP events bracket
+        # both; flops and traffic are those of the whole projection.
+        roof = {"bound": "mfma",
+                "kernel": "gemm_bf16_kernel: gate/up projection with RMSNorm scaling and SiLU.up fused "
+                          "(256x256 16x16x32-MFMA launch + 256x128 tail launch)",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "flops_per_launch": fl[dom], "avg_launch_ms": round(st[dom], 5),
+                "flops_per_call": fl[dom], "avg_call_ms": round(st[dom], 5),
+                "launches_per_projection": 2,
                 "traffic": traffic_from_profile("gate_up_8b_prefill")}
     else:
         by = stage_bytes(wl)
@@ -292,7 +301,8 @@ def main():
         for other, sets in (("8b_bf16_decode", 2), ("70b_bf16_decode", 2), ("8b_bf16_chunked_prefill", 1),
                             ("70b_bf16_prefill", 1)):
             steps = max(3, args.steps // 4) if other == "70b_bf16_prefill" else args.steps
-            owl, oms, ost = time_workload(other, steps, max(2, args.warmup // 2), sets=sets)
+            owl, oms, ost = time_workload(other, steps, max(2, args.warmup // 2), sets=sets,
+                                          warm_seconds=args.warmup_seconds)
             others[other] = summarize(owl, oms, ost)
             log(f"{other}: {oms:.3f} ms/step")
         result["other_workloads"] = others
