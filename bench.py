@@ -11,8 +11,9 @@ reports:
     FLOPs per launch over its average launch time, measured with HIP events on
     the launch stream over the timed region, against the bf16 MFMA peak;
   * cpu_baseline: the fp64 CPU oracle timed on the host on the same workload;
-  * other_workloads: 8B decode (B=32, P=1000), 70B decode (B=64, P=4096), 8B
-    chunked prefill (B=1, T=2048 at start 2048) and 70B prefill (B=1, T=16384),
+  * other_workloads: 8B decode (B=32, P=1000), 70B decode (B=64, P=4096), 8B ragged
+    decode (B=32, start positions spread over 0..2000), 8B chunked prefill (B=1,
+    T=2048 at start 2048) and 70B prefill (B=1, T=16384),
     each timed the same way (decode with two weight and
     cache sets used alternately so that the 256 MB last-level cache cannot hold
     the working set between steps), with per-stage times.
@@ -44,11 +45,14 @@ def log(msg):
 def stage_flops(wl):
     """Algorithmic FLOPs per stage: 2 per multiply-add of each projection; attention
     4*hd*n_heads per visible (query, key) pair (Q.K and P.V), causal pairs only."""
+    import workloads
     s = wl.shape
     M = wl.B * wl.T
     d, hd, f = s.d_model, s.head_dim, s.d_ff
     if wl.mode == "prefill":
         pairs = wl.B * (wl.T * wl.P + wl.T * (wl.T + 1) // 2)
+    elif wl.ragged:
+        pairs = sum(p + 1 for p in workloads.ragged_positions(wl))
     else:
         pairs = wl.B * (wl.P + 1)
     return {
@@ -63,6 +67,7 @@ def stage_flops(wl):
 def stage_bytes(wl):
     """Algorithmic HBM bytes per stage: each weight once, norm gains, KV rows read
     (P cached rows) and written (new rows), x read and y written."""
+    import workloads
     s = wl.shape
     es = 2 if s.dtype == "bf16" else 4
     M = wl.B * wl.T
@@ -70,7 +75,7 @@ def stage_bytes(wl):
     kv_row = s.n_kv_heads * hd * es
     return {
         "qkv": (s.n_heads + 2 * s.n_kv_heads) * hd * d * es + d * es + M * d * 4 + 2 * M * kv_row,
-        "attention": 2 * wl.B * wl.P * kv_row,
+        "attention": 2 * kv_row * (sum(workloads.ragged_positions(wl)) if wl.ragged else wl.B * wl.P),
         "o_proj": d * s.n_heads * hd * es,
         "gate_up": 2 * f * d * es + d * es,
         "down": d * f * es + M * d * 4,
@@ -86,7 +91,7 @@ def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
     wl = workloads.get(name)
     shp = wl.shape
     dev = "cuda"
-    cap = workloads.cache_capacity(wl.P + wl.T)
+    cap = workloads.cache_capacity(workloads.max_start(wl) + wl.T)
     log(f"{name}: building {sets} weight/cache set(s) on the GPU")
     blocks, caches = [], []
     w, gen = workloads.make_weights(shp, wl.seed, device=dev)
@@ -95,11 +100,12 @@ def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
         blocks.append(llb.llb_block_create(llb.make_config(shp, cap), w))
         if tiles is not None:
             llb.llb_block_set_tiles(blocks[-1], *tiles)
-        kc, vc = workloads.make_cache(shp, wl.B, wl.P, cap, gen, device=dev)
+        kc, vc = workloads.make_cache(shp, wl.B, workloads.max_start(wl), cap, gen, device=dev)
         caches.append((kc, vc))
     del w
     y = torch.empty_like(x)
     ws = llb.workspace(blocks[0], wl.B, wl.T)
+    positions = workloads.ragged_positions(wl) if wl.ragged else None
     torch.cuda.synchronize()
 
     def step(i):
@@ -109,6 +115,8 @@ def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
             llb.llb_block_prefill_at(blk, x, y, wl.B, wl.T, wl.P, kc, vc, cap, ws)
         elif wl.mode == "prefill":
             llb.llb_block_prefill(blk, x, y, wl.B, wl.T, kc, vc, cap, ws)
+        elif wl.ragged:
+            llb.llb_block_decode_ragged(blk, x, y, wl.B, positions, kc, vc, cap, ws)
         else:
             llb.llb_block_decode(blk, x, y, wl.B, wl.P, kc, vc, cap, ws)
 
@@ -298,8 +306,8 @@ def main():
 
     if not args.no_others and args.only is None:
         others = {}
-        for other, sets in (("8b_bf16_decode", 2), ("70b_bf16_decode", 2), ("8b_bf16_chunked_prefill", 1),
-                            ("70b_bf16_prefill", 1)):
+        for other, sets in (("8b_bf16_decode", 2), ("70b_bf16_decode", 2), ("8b_bf16_ragged_decode", 2),
+                            ("8b_bf16_chunked_prefill", 1), ("70b_bf16_prefill", 1)):
             steps = max(3, args.steps // 4) if other == "70b_bf16_prefill" else args.steps
             owl, oms, ost = time_workload(other, steps, max(2, args.warmup // 2), sets=sets,
                                           warm_seconds=args.warmup_seconds)

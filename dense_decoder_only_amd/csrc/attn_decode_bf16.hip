@@ -203,7 +203,7 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
     const int bg = wid / n_chunks;
     const int g = bg % a.n_kv;
     const int b = bg / a.n_kv;
-    const int L = a.pos0 + 1;
+    const int L = (a.pos_b ? a.pos_b[b] : a.pos0) + 1;
     const int k_beg = ci * chunk;
     const int k_end = min(L, k_beg + chunk);
     float o[G][8], m_run, l_run;
@@ -242,7 +242,7 @@ attn_decode_fused_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int g = blockIdx.x % a.n_kv;
     const int b = blockIdx.x / a.n_kv;
-    const int L = a.pos0 + 1;
+    const int L = (a.pos_b ? a.pos_b[b] : a.pos0) + 1;
     const int chunk = ((L + AD_FW - 1) / AD_FW + 15) / 16 * 16;
     const int k_beg = min(L, wave * chunk);
     const int k_end = min(L, k_beg + chunk);

@@ -405,7 +405,7 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
 
 hipError_t attn_prefill_bf16_launch(const AttnArgs& a, hipStream_t s) {
     if (a.hd != AP_HD || a.n_kv <= 0 || a.n_heads % a.n_kv != 0 || a.T <= 0 || a.B <= 0 ||
-        a.pos0 < 0 || a.pos0 + a.T > a.cap)
+        a.pos0 < 0 || a.pos0 + a.T > a.cap || a.pos_b != nullptr)
         return hipErrorInvalidValue;
     switch (a.n_heads / a.n_kv) {
         case 1: return launch_g<1, 2, 2>(a, s);

@@ -166,7 +166,7 @@ hipError_t stage_event(llb_block* b, hipStream_t s) {
 }
 
 struct WsPlan {
-    size_t q = 0, o = 0, h = 0, u = 0, a1 = 0, a2 = 0, ssq1 = 0, ssq2 = 0, scratch = 0, total = 0;
+    size_t q = 0, o = 0, h = 0, u = 0, a1 = 0, a2 = 0, ssq1 = 0, ssq2 = 0, pos = 0, scratch = 0, total = 0;
     size_t scratch_bytes = 0;
 };
 
@@ -203,6 +203,10 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
         }
         const size_t att = llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys);
         if (att > scratch) scratch = att;
+    }
+    if (decode) {  // per-sequence start positions of a ragged decode call
+        p.pos = off;
+        off += align_up((size_t)B * sizeof(int32_t));
     }
     p.scratch = off;
     p.scratch_bytes = scratch;
@@ -294,8 +298,11 @@ llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, fl
 // The kernel sequence of one block call over M = B*T tokens at positions
 // pos0..pos0+T-1 ("Llama 3.1 70B", section "Transformer layer"):
 //   h = x + Wo . Attn(RMSNorm(x)),  y = h + Wdown . SwiGLU(RMSNorm(h)).
+// pos_host: per-sequence start positions (host, B entries; T = 1), or null:
+// every sequence starts at pos0.  With them, pos0 is their maximum.
 llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int pos0, void* kc,
-                     void* vc, int cap, void* ws, size_t ws_bytes, hipStream_t s, bool decode) {
+                     void* vc, int cap, void* ws, size_t ws_bytes, hipStream_t s, bool decode,
+                     const int32_t* pos_host = nullptr) {
     const llb_config& c = b->cfg;
     const int L = pos0 + T;
     const WsPlan p = plan_ws(b, B, T, decode, L);
@@ -333,9 +340,19 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
                             k.cfg, k.N, k.K);
     }
 
+    const int* pos_b = nullptr;
+    if (pos_host) {
+        // the positions travel to the workspace in kernel arguments, ahead of the
+        // kernels that read them
+        pos_b = (const int*)(w + p.pos);
+        const hipError_t ce = llb::store_ints_launch((int*)pos_b, pos_host, B, s);
+        if (ce != hipSuccess) return hip_fail(ce, "start positions");
+    }
+
     llb::Epilogue e{};
     e.rope = b->rope;
     e.T = T; e.pos0 = pos0; e.cap = cap; e.n_heads = c.n_heads; e.n_kv = c.n_kv_heads; e.hd = hd;
+    e.pos_b = pos_b;
 
     hipError_t te = stage_event(b, s);
     if (te != hipSuccess) return hip_fail(te, "stage timing");
@@ -359,6 +376,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     llb::AttnArgs at{};
     at.q = q; at.k_cache = kc; at.v_cache = vc; at.o = o; at.B = B; at.T = T; at.pos0 = pos0;
     at.cap = cap; at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads; at.hd = hd;
+    at.pos_b = pos_b;
     hipError_t he;
     if (!bf16) he = llb::attn_f32_launch(at, s);
     else if (decode) he = llb::attn_decode_bf16_launch(at, scratch, s);
@@ -601,6 +619,26 @@ llb_status llb_block_decode(llb_block* b, const float* x, float* y, int32_t B, i
                     b->cfg.max_positions);
     return run_block(b, x, y, B, 1, start_pos, k_cache, v_cache, cache_cap, ws, ws_bytes,
                      (hipStream_t)stream, true);
+}
+
+llb_status llb_block_decode_ragged(llb_block* b, const float* x, float* y, int32_t B,
+                                   const int32_t* start_pos, void* k_cache, void* v_cache,
+                                   int32_t cache_cap, void* ws, size_t ws_bytes, void* stream) {
+    llb_status st = check_call(b, x, y, B, 1, k_cache, v_cache, cache_cap, ws);
+    if (st != LLB_OK) return st;
+    if (!start_pos) return fail(LLB_E_INVALID, "start_pos is NULL");
+    int max_pos = 0;
+    for (int i = 0; i < B; ++i) {
+        const int p = start_pos[i];
+        if (p < 0) return fail(LLB_E_INVALID, "start_pos[%d]=%d must be >= 0", i, p);
+        if (p + 1 > cache_cap)
+            return fail(LLB_E_CAPACITY, "start_pos[%d]+1=%d exceeds cache_cap=%d", i, p + 1, cache_cap);
+        if (p >= b->cfg.max_positions)
+            return fail(LLB_E_CAPACITY, "start_pos[%d]=%d >= max_positions=%d", i, p, b->cfg.max_positions);
+        max_pos = std::max(max_pos, p);
+    }
+    return run_block(b, x, y, B, 1, max_pos, k_cache, v_cache, cache_cap, ws, ws_bytes,
+                     (hipStream_t)stream, true, start_pos);
 }
 
 llb_status llb_kv_append(const llb_block* b, void* k_cache, void* v_cache, int32_t B,

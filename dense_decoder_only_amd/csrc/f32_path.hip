@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
     const int hd = a.hd;
     const int G = a.n_heads / a.n_kv;
     const int g = h / G;
-    const int pos = a.pos0 + t;
+    const int pos = (a.pos_b ? a.pos_b[b] : a.pos0) + t;
     const int L = pos + 1;
     const float* q = (const float*)a.q + (((size_t)b * a.n_heads + h) * a.T + t) * hd;
     const size_t head_off = ((size_t)b * a.n_kv + g) * a.cap * hd;
@@ -189,6 +189,30 @@ hipError_t attn_f32_launch(const AttnArgs& a, hipStream_t s) {
     if (a.hd > 128 || a.n_kv <= 0 || a.n_heads % a.n_kv != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.T, a.n_heads, a.B), dim3(64), 0, s, a);
     return hipGetLastError();
+}
+
+namespace {
+// Up to 64 host integers carried in the kernel's arguments (copied at launch,
+// so the host array is free as soon as the launch returns).
+struct IntChunk {
+    int n;
+    int v[64];
+};
+__global__ void __launch_bounds__(64) store_ints_kernel(int* __restrict__ dst, IntChunk c) {
+    if ((int)threadIdx.x < c.n) dst[threadIdx.x] = c.v[threadIdx.x];
+}
+}  // namespace
+
+hipError_t store_ints_launch(int* dst, const int* src, int n, hipStream_t s) {
+    for (int i = 0; i < n; i += 64) {
+        IntChunk c;
+        c.n = n - i < 64 ? n - i : 64;
+        for (int j = 0; j < c.n; ++j) c.v[j] = src[i + j];
+        hipLaunchKernelGGL(store_ints_kernel, dim3(1), dim3(64), 0, s, dst + i, c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t kv_append_launch(void* kc, void* vc, const void* kn, const void* vn, int B, int n_kv,

@@ -21,6 +21,9 @@ struct Epilogue {
     void* v_cache;
     const float2* rope;
     int T, pos0, cap, n_heads, n_kv, hd;
+    // Per-sequence start positions [B] (device; decode with T = 1), or null:
+    // every sequence starts at pos0.
+    const int* pos_b;
     // EPI_RESID: out[m, n] = resid[m, n] + C[m, n]   (fp32, [M, N] row-major)
     const float* resid;
     float* out;
@@ -96,6 +99,9 @@ struct AttnArgs {
     const void* v_cache;
     void* o;              // [B, T, n_heads*hd]
     int B, T, pos0, cap, n_heads, n_kv, hd;
+    // Per-sequence start positions [B] (device), or null: all start at pos0.  With
+    // them, pos0 is their maximum (it sizes the work split).
+    const int* pos_b;
 };
 hipError_t attn_prefill_bf16_launch(const AttnArgs& a, hipStream_t s);
 // Split-K decode attention + merge.  ws: attn_decode_ws_bytes(...) bytes.
@@ -105,6 +111,9 @@ hipError_t attn_decode_bf16_launch(const AttnArgs& a, float* ws, hipStream_t s);
 hipError_t attn_f32_launch(const AttnArgs& a, hipStream_t s);
 
 // ---- cache helpers ---------------------------------------------------------
+// dst[0..n) = src[0..n) (src on the host), through kernel arguments: ordered on
+// stream s like the kernels, and src may be reused as soon as this returns.
+hipError_t store_ints_launch(int* dst, const int* src, int n, hipStream_t s);
 hipError_t kv_append_launch(void* kc, void* vc, const void* kn, const void* vn, int B, int n_kv,
                             int cap, int pos0, int n_new, int hd, int elem_bytes, hipStream_t s);
 

@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "LLB_OK", -1: "LLB_E_INVALID", -2: "LLB_E_UNSUPPORTED", -3: "
                 -4: "LLB_E_HIP", -5: "LLB_E_NOMEM"}
 
 EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes",
-            "llb_block_prefill", "llb_block_prefill_at", "llb_block_decode", "llb_kv_append", "llb_attention_prefill",
+            "llb_block_prefill", "llb_block_prefill_at", "llb_block_decode", "llb_block_decode_ragged", "llb_kv_append", "llb_attention_prefill",
             "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
             "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles",
             "llb_last_error")
@@ -85,6 +85,8 @@ def load_library(path: str = LIB_PATH):
     lib.llb_block_prefill_at.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, sz, vp]
     lib.llb_block_prefill_at.restype = ctypes.c_int
     lib.llb_block_decode.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, vp, sz, vp]
+    lib.llb_block_decode_ragged.argtypes = [vp, vp, vp, i32, ctypes.POINTER(i32), vp, vp, i32, vp, sz, vp]
+    lib.llb_block_decode_ragged.restype = ctypes.c_int
     lib.llb_block_decode.restype = ctypes.c_int
     lib.llb_kv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.llb_kv_append.restype = ctypes.c_int
@@ -196,6 +198,17 @@ def llb_block_decode(blk: Block, x, y, B, start_pos, k_cache, v_cache, cache_cap
     _check(load_library().llb_block_decode(blk.handle, _ptr(x), _ptr(y), B, start_pos, _ptr(k_cache),
                                            _ptr(v_cache), cache_cap, _ptr(ws), ws.numel() * ws.element_size(),
                                            _stream(stream)), "llb_block_decode")
+
+
+def llb_block_decode_ragged(blk: Block, x, y, B, start_pos, k_cache, v_cache, cache_cap, ws, stream=None):
+    """start_pos: B host integers (a list or a CPU tensor), one position per sequence."""
+    if len(start_pos) != B:
+        raise ValueError("start_pos must have B entries")
+    pos = (ctypes.c_int32 * B)(*[int(p) for p in start_pos])
+    _check(load_library().llb_block_decode_ragged(blk.handle, _ptr(x), _ptr(y), B, pos, _ptr(k_cache),
+                                                  _ptr(v_cache), cache_cap, _ptr(ws),
+                                                  ws.numel() * ws.element_size(), _stream(stream)),
+           "llb_block_decode_ragged")
 
 
 def llb_kv_append(blk: Block, k_cache, v_cache, B, cache_cap, start_pos, n_new, k_new, v_new,

@@ -143,6 +143,19 @@ llb_status llb_block_decode(llb_block* blk, const float* x, float* y, int32_t B,
                             void* k_cache, void* v_cache, int32_t cache_cap,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Ragged decode: as llb_block_decode, but sequence b's new token sits at its
+ * own position start_pos[b] and attends to its cache rows 0..start_pos[b]
+ * (L_b = start_pos[b] + 1 keys; the pages give one start position per call, a
+ * batch of different lengths is this library's extension).  start_pos is a
+ * HOST array of B entries, read during the call (it reaches the device in
+ * kernel arguments, so the caller may reuse it once the call returns).  Writes cache row
+ * start_pos[b] of sequence b.  Workspace: llb_block_workspace_bytes(blk, B, 1).
+ * Needs every start_pos[b] >= 0, start_pos[b] + 1 <= cache_cap and
+ * start_pos[b] < max_positions; a violation fails before anything is queued. */
+llb_status llb_block_decode_ragged(llb_block* blk, const float* x, float* y, int32_t B,
+                                   const int32_t* start_pos, void* k_cache, void* v_cache,
+                                   int32_t cache_cap, void* ws, size_t ws_bytes, void* stream);
+
 /* Copies k_new, v_new [B, n_kv_heads, n_new, head_dim] (wdtype) into cache
  * rows start_pos..start_pos+n_new-1 of every sequence and KV head.  Used to
  * seed caches.  Needs start_pos + n_new <= cache_cap. */

@@ -197,6 +197,97 @@ def test_bf16_decode_small(B, P, G):
     assert torch.all(kd[:, :, P + 1:].float() == SENTINEL)
 
 
+def _ragged_positions(B, P_max, seed):
+    g = torch.Generator().manual_seed(seed)
+    pos = torch.randint(0, P_max + 1, (B,), generator=g).tolist()
+    pos[0] = 0                     # an empty prefix
+    pos[-1] = P_max                # the longest sequence
+    return pos
+
+
+@pytest.mark.parametrize("B,P_max,Hkv,G,dtype", [
+    (5, 300, 2, 4, "bf16"),     # split-over-workgroups attention, weight-streaming projections
+    (40, 200, 4, 4, "bf16"),    # one workgroup per (sequence, KV head)
+    (70, 150, 2, 8, "bf16"),    # M = 70: the projections run as GEMM tiles
+    (6, 90, 2, 4, "f32"),
+])
+def test_ragged_decode(B, P_max, Hkv, G, dtype):
+    """Every sequence decodes one token at its own position: y row b against the
+    oracle run on sequence b alone at start position P_b; only cache row P_b of
+    sequence b changes (rows past it hold the sentinel and must stay unread)."""
+    from dense_decoder_only_amd import llb
+    shp = shape(d_model=512, n_heads=G * Hkv, n_kv_heads=Hkv, head_dim=128 if dtype == "bf16" else 64,
+                d_ff=768, rope_scaling=(G == 8), dtype=dtype)
+    pos = _ragged_positions(B, P_max, 7 + B)
+    cap = workloads.cache_capacity(P_max + 1)
+    w, x, kc, vc = gen_inputs(shp, 13 + B, B, 1, P_max, cap, fill=SENTINEL)
+    for b, p in enumerate(pos):                       # rows >= P_b: sentinel
+        kc[b, :, p:] = SENTINEL
+        vc[b, :, p:] = SENTINEL
+    note(f"ragged decode {dtype} B={B} positions {min(pos)}..{max(pos)}")
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        kd, vd = kc.cuda(), vc.cuda()
+        y = torch.empty(B, 1, shp.d_model, device="cuda")
+        llb.llb_block_decode_ragged(gb.blk, x.cuda(), y, B, pos, kd, vd, cap, gb.workspace(B, 1))
+        y, kd, vd = y.cpu(), kd.cpu(), vd.cpu()
+    finally:
+        gb.close()
+    bar = 2e-2 if dtype == "bf16" else 1e-5
+    worst_y, worst_k = 0.0, 0.0
+    for b, p in enumerate(pos):
+        y_ref, k_ref, v_ref = oracle.block_forward(shp, w, x[b:b + 1], kc[b:b + 1], vc[b:b + 1], p)
+        worst_y = max(worst_y, rel_err(y[b:b + 1], y_ref))
+        if dtype == "bf16":
+            worst_k = max(worst_k, bf16_err(kd[b:b + 1, :, p:p + 1], k_ref), bf16_err(vd[b:b + 1, :, p:p + 1], v_ref))
+        else:
+            worst_k = max(worst_k, rel_err(kd[b:b + 1, :, p:p + 1], k_ref))
+        assert torch.equal(kd[b, :, :p], kc[b, :, :p]) and torch.equal(vd[b, :, :p], vc[b, :, :p])
+        assert torch.all(kd[b, :, p + 1:].float() == SENTINEL)
+    note(f"  worst y {worst_y:.2e}  worst k/v {worst_k:.3f}")
+    assert worst_y <= bar
+    assert worst_k <= (1.0 if dtype == "bf16" else 1e-5)
+
+
+def test_ragged_decode_with_equal_positions_is_decode():
+    from dense_decoder_only_amd import llb
+    shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+    B, P = 9, 77
+    cap = workloads.cache_capacity(P + 1)
+    w, x, kc, vc = gen_inputs(shp, 17, B, 1, P, cap)
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        k1, v1, k2, v2 = kc.cuda(), vc.cuda(), kc.cuda(), vc.cuda()
+        y1 = gb.decode(x.cuda(), k1, v1, P)
+        y2 = torch.empty_like(y1)
+        llb.llb_block_decode_ragged(gb.blk, x.cuda(), y2, B, [P] * B, k2, v2, cap, gb.workspace(B, 1))
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(k1, k2) and torch.equal(v1, v2)
+    finally:
+        gb.close()
+
+
+def test_ragged_decode_rejects_bad_positions():
+    from dense_decoder_only_amd import llb
+    shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+    B, cap = 3, 64
+    w, x, kc, vc = gen_inputs(shp, 19, B, 1, 10, cap)
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        kd, vd = kc.cuda(), vc.cuda()
+        y = torch.empty(B, 1, shp.d_model, device="cuda")
+        for pos, status in (([0, -1, 3], llb.LLB_E_INVALID), ([0, 64, 3], llb.LLB_E_CAPACITY)):
+            with pytest.raises(llb.LlbError) as ei:
+                llb.llb_block_decode_ragged(gb.blk, x.cuda(), y, B, pos, kd, vd, cap, gb.workspace(B, 1))
+            assert ei.value.status == status
+        with pytest.raises(ValueError):
+            llb.llb_block_decode_ragged(gb.blk, x.cuda(), y, B, [1, 2], kd, vd, cap, gb.workspace(B, 1))
+        torch.cuda.synchronize()
+        assert torch.equal(kd.cpu(), kc)
+    finally:
+        gb.close()
+
+
 def test_bf16_prefill_then_decode_matches_longer_prefill():
     """GPU prefill(T) fills the cache; GPU decode at P = T must equal row T of the
     oracle's prefill(T + 1) (the oracle never sees GPU data)."""

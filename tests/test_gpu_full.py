@@ -4,6 +4,8 @@ bench.py times (same entry points, shapes and dtypes).
   * 8B prefill (B=1, T=2048), 8B chunked prefill (B=1, T=2048 at start 2048) and
     8B decode (B=32, P=1000): every output row.
   * 70B decode (B=64, P=4096, llama3-scaled RoPE): every output row.
+  * 8B ragged decode (B=32, start positions spread over 0..2000): every row, each
+    against the oracle on its own sequence.
   * 70B long prefill (B=1, T=16384): keys/values for all 16384 tokens are checked
     against the oracle; y on a fixed set of sampled rows (first, last, tile edges),
     which the oracle computes one by one (a causal block's row t depends only on
@@ -26,7 +28,7 @@ C5_ROWS = [0, 1, 31, 32, 63, 64, 255, 256, 1000, 4095, 4096, 8191, 8192, 12345, 
 
 
 def _inputs(wl):
-    cap = workloads.cache_capacity(wl.P + wl.T)
+    cap = workloads.cache_capacity(workloads.max_start(wl) + wl.T)
     return workloads.make_inputs(wl, cap=cap)
 
 
@@ -85,3 +87,34 @@ def test_full_decode(name):
     assert e_y <= 2e-2
     assert e_k <= 1.0 and e_v <= 1.0
     assert torch.equal(kd[:, :, :wl.P], inp["k_cache"][:, :, :wl.P])
+
+
+def test_full_ragged_decode():
+    """8B ragged decode (B=32, start positions spread over 0..2000): every row
+    against the oracle run on its own sequence at its own position."""
+    from dense_decoder_only_amd import llb
+    wl = workloads.get("8b_bf16_ragged_decode")
+    pos = workloads.ragged_positions(wl)
+    note("full 8b_bf16_ragged_decode: generating inputs")
+    inp = _inputs(wl)
+    cap = inp["cap"]
+    gb = GpuBlock(wl.shape, inp["weights"], max_positions=cap)
+    try:
+        kd, vd = inp["k_cache"].cuda(), inp["v_cache"].cuda()
+        y = torch.empty(wl.B, 1, wl.shape.d_model, device="cuda")
+        note(f"full 8b_bf16_ragged_decode: GPU decode B={wl.B} positions {min(pos)}..{max(pos)}")
+        llb.llb_block_decode_ragged(gb.blk, inp["x"].cuda(), y, wl.B, pos, kd, vd, cap, gb.workspace(wl.B, 1))
+        torch.cuda.synchronize()
+        y, kd, vd = y.cpu(), kd.cpu(), vd.cpu()
+    finally:
+        gb.close()
+    note("full 8b_bf16_ragged_decode: oracle per sequence")
+    e_y = e_k = 0.0
+    for b, p in enumerate(pos):
+        sl = slice(b, b + 1)
+        y_ref, k_ref, v_ref = oracle.block_forward(wl.shape, inp["weights"], inp["x"][sl], inp["k_cache"][sl],
+                                                   inp["v_cache"][sl], p)
+        e_y = max(e_y, rel_err(y[sl], y_ref))
+        e_k = max(e_k, bf16_err(kd[sl, :, p:p + 1], k_ref), bf16_err(vd[sl, :, p:p + 1], v_ref))
+    note(f"full 8b_bf16_ragged_decode: worst y {e_y:.3e} worst k/v {e_k:.3f}")
+    assert e_y <= 2e-2 and e_k <= 1.0

@@ -91,6 +91,7 @@ class Workload:
     T: int = 1         # new tokens per sequence (1 for decode)
     P: int = 0         # cached positions before the call (start position)
     seed: int = 0
+    ragged: bool = False  # decode: sequence b starts at ragged_positions(self)[b] (mean P)
 
     @property
     def tokens(self) -> int:
@@ -108,6 +109,9 @@ CONFIGS: Dict[str, Workload] = {
     "8b_bf16_decode": Workload("8b_bf16_decode", LLAMA31_8B, "decode", B=32, T=1, P=1000, seed=3),
     "70b_bf16_decode": Workload("70b_bf16_decode", LLAMA31_70B, "decode", B=64, T=1, P=4096, seed=4),
     "70b_bf16_prefill": Workload("70b_bf16_prefill", LLAMA31_70B, "prefill", B=1, T=16384, seed=5),
+    # 32 sequences of different lengths, evenly spread over 0..2P (mean P = 1000)
+    "8b_bf16_ragged_decode": Workload("8b_bf16_ragged_decode", LLAMA31_8B, "decode", B=32, T=1, P=1000,
+                                      seed=7, ragged=True),
     # second 2048-token chunk of a 4096-token prompt: positions 2048..4095 over a
     # 2048-row cache prefix
     "8b_bf16_chunked_prefill": Workload("8b_bf16_chunked_prefill", LLAMA31_8B, "prefill", B=1, T=2048,
@@ -166,6 +170,16 @@ def make_x(B: int, T: int, d: int, gen: torch.Generator, device="cpu") -> torch.
     return _randn((B, T, d), gen, device)
 
 
+def ragged_positions(wl: Workload):
+    """Start positions of a ragged decode workload: sequence b at
+    round((2b + 1) P / B), evenly spread over 0..2P (mean P)."""
+    return [int(round((2 * b + 1) * wl.P / wl.B)) for b in range(wl.B)]
+
+
+def max_start(wl: Workload) -> int:
+    return max(ragged_positions(wl)) if wl.ragged else wl.P
+
+
 def make_cache(shape: BlockShape, B: int, P: int, cap: int, gen: torch.Generator, device="cpu",
                fill=0.0):
     """K and V caches [B, n_kv, cap, hd]; rows 0..P-1 ~ N(0,1), rows P.. = `fill`."""
@@ -183,6 +197,6 @@ def make_inputs(wl: Workload, device="cpu", cap: Optional[int] = None):
     w, gen = make_weights(wl.shape, wl.seed, device)
     x = make_x(wl.B, wl.T, wl.shape.d_model, gen, device)
     if cap is None:
-        cap = cache_capacity(wl.P + wl.T)
-    kc, vc = make_cache(wl.shape, wl.B, wl.P, cap, gen, device)
+        cap = cache_capacity(max_start(wl) + wl.T)
+    kc, vc = make_cache(wl.shape, wl.B, max_start(wl), cap, gen, device)
     return {"weights": w, "x": x, "k_cache": kc, "v_cache": vc, "cap": cap}
