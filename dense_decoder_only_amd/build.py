@@ -25,6 +25,7 @@ SOURCES = [
     "attn_prefill_bf16.hip",
     "attn_decode_bf16.hip",
     "f32_path.hip",
+    "model_kernels.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -429,6 +429,28 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     return LLB_OK;
 }
 
+// fp32 copy of a gain vector of d elements (es bytes each, on the device).
+hipError_t widen_gain(const void* src, float* dst, size_t d, size_t es, hipStream_t s) {
+    std::vector<unsigned char> raw(d * es);
+    std::vector<float> f(d);
+    hipError_t e = hipMemcpyAsync(raw.data(), src, d * es, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    for (size_t i = 0; i < d; ++i) {
+        if (es == 4) {
+            std::memcpy(&f[i], &raw[4 * i], 4);
+        } else {
+            uint16_t hbits;
+            std::memcpy(&hbits, &raw[2 * i], 2);
+            const uint32_t u = (uint32_t)hbits << 16;
+            std::memcpy(&f[i], &u, 4);
+        }
+    }
+    e = hipMemcpyAsync(dst, f.data(), d * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -753,6 +775,188 @@ llb_status llb_block_stage_times(llb_block* b, float* ms, int32_t* n_calls) {
     }
     *n_calls = (int32_t)calls;
     b->events_used = 0;
+    return LLB_OK;
+}
+
+
+// ---- model: embedding, n_layers blocks, final RMSNorm, LM head ---------------
+
+struct llb_model {
+    uint32_t magic;
+    llb_config cfg;
+    int n_layers, vocab;
+    std::vector<llb_block*> layers;
+    void* embed;   // [vocab, d] bf16, row-major
+    float* gain;   // [d] fp32
+    void* head;    // [vocab, d] bf16, 128 x 64 tiled layout
+};
+
+static constexpr uint32_t kModelMagic = 0x4c4c4d44u, kModelDead = 0x44454144u;
+
+static bool model_ok(const llb_model* m) { return m != nullptr && m->magic == kModelMagic; }
+
+static void free_model(llb_model* m) {
+    for (llb_block* b : m->layers) llb_block_destroy(b);
+    m->layers.clear();
+    if (m->embed) (void)hipFree(m->embed);
+    if (m->gain) (void)hipFree(m->gain);
+    if (m->head) (void)hipFree(m->head);
+    m->embed = m->head = nullptr;
+    m->gain = nullptr;
+}
+
+llb_status llb_model_create(const llb_config* cfg, int32_t n_layers, int32_t vocab, const void* embed,
+                            const llb_weights* layers, const void* final_norm, const void* lm_head,
+                            void* stream, llb_model** out) {
+    if (!out) return fail(LLB_E_INVALID, "out is NULL");
+    *out = nullptr;
+    llb_status st = check_config(cfg);
+    if (st != LLB_OK) return st;
+    if (cfg->wdtype != LLB_BF16) return fail(LLB_E_UNSUPPORTED, "models need bf16 weights");
+    if (n_layers < 0) return fail(LLB_E_INVALID, "n_layers must be >= 0");
+    if (vocab <= 0 || vocab % 128 != 0) return fail(LLB_E_UNSUPPORTED, "vocab %d must be a positive multiple of 128", vocab);
+    if (!embed || !final_norm || !lm_head || (n_layers > 0 && !layers))
+        return fail(LLB_E_INVALID, "a weight pointer is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    llb_model* m = new (std::nothrow) llb_model();
+    if (!m) return fail(LLB_E_NOMEM, "host allocation failed");
+    m->cfg = *cfg;
+    m->n_layers = n_layers;
+    m->vocab = vocab;
+    for (int l = 0; l < n_layers; ++l) {
+        llb_block* b = nullptr;
+        st = llb_block_create(cfg, &layers[l], stream, &b);
+        if (st != LLB_OK) {
+            free_model(m);
+            delete m;
+            return st;
+        }
+        m->layers.push_back(b);
+    }
+    const size_t d = cfg->d_model, V = vocab, mat = V * d * 2;
+    hipError_t e = hipMalloc(&m->embed, mat);
+    if (e == hipSuccess) e = hipMalloc(&m->head, mat);
+    if (e == hipSuccess) e = hipMalloc((void**)&m->gain, d * 4);
+    if (e != hipSuccess) {
+        free_model(m);
+        delete m;
+        return fail(LLB_E_NOMEM, "hipMalloc of the embedding / head failed: %s", hipGetErrorString(e));
+    }
+    e = hipMemcpyAsync(m->embed, embed, mat, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = llb::tile_weights_launch(lm_head, m->head, (int)V, (int)d, s);
+    if (e == hipSuccess) e = widen_gain(final_norm, m->gain, d, 2, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        free_model(m);
+        delete m;
+        return hip_fail(e, "model weight upload");
+    }
+    m->magic = kModelMagic;
+    *out = m;
+    return LLB_OK;
+}
+
+llb_status llb_model_destroy(llb_model* m) {
+    if (!m) return LLB_OK;
+    if (m->magic != kModelMagic) return fail(LLB_E_INVALID, "not a live model handle");
+    (void)hipDeviceSynchronize();
+    free_model(m);
+    m->magic = kModelDead;
+    delete m;
+    return LLB_OK;
+}
+
+namespace {
+struct ModelWs {
+    size_t x = 0, blk = 0, blk_bytes = 0, xl = 0, a = 0, ssq = 0, scratch = 0, scratch_bytes = 0, total = 0;
+};
+ModelWs plan_model_ws(const llb_model* m, int B, int T, bool last_only) {
+    ModelWs p;
+    const size_t d = m->cfg.d_model;
+    const int M = B * T, R = (last_only && T > 1) ? B : M;
+    size_t off = 0;
+    p.x = off; off += align_up((size_t)M * d * 4);
+    p.blk_bytes = m->n_layers > 0 ? llb_block_workspace_bytes(m->layers[0], B, T) : 0;
+    p.blk = off; off += align_up(p.blk_bytes);
+    if (R != M) { p.xl = off; off += align_up((size_t)R * d * 4); }
+    p.a = off; off += align_up((size_t)R * d * 2);
+    p.ssq = off; off += align_up((size_t)R * 4);
+    if (R <= 64) {
+        const int sp = llb::gemv_bf16_splits(R, m->vocab, (int)d);
+        p.scratch_bytes = llb::gemv_bf16_ws_bytes(R, m->vocab, sp);
+    }
+    p.scratch = off; off += align_up(p.scratch_bytes);
+    p.total = off;
+    return p;
+}
+}  // namespace
+
+size_t llb_model_workspace_bytes(const llb_model* m, int32_t B, int32_t T, int32_t last_only) {
+    if (!model_ok(m) || B <= 0 || T <= 0) return 0;
+    return plan_model_ws(m, B, T, last_only != 0).total;
+}
+
+llb_status llb_model_forward(llb_model* m, const int32_t* tokens, int32_t B, int32_t T, int32_t start_pos,
+                             void* const* k_caches, void* const* v_caches, int32_t cache_cap,
+                             int32_t last_only, float* logits, void* ws, size_t ws_bytes, void* stream) {
+    if (!model_ok(m)) return fail(LLB_E_INVALID, "not a live model handle");
+    if (!tokens || !logits || !ws) return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (B <= 0 || T <= 0) return fail(LLB_E_INVALID, "B and T must be positive");
+    if (start_pos < 0) return fail(LLB_E_INVALID, "start_pos must be >= 0");
+    if (m->n_layers > 0) {
+        if (!k_caches || !v_caches) return fail(LLB_E_INVALID, "cache arrays are NULL");
+        for (int l = 0; l < m->n_layers; ++l)
+            if (!k_caches[l] || !v_caches[l]) return fail(LLB_E_INVALID, "cache of layer %d is NULL", l);
+        if ((long)start_pos + T > cache_cap)
+            return fail(LLB_E_CAPACITY, "start_pos+T=%ld exceeds cache_cap=%d", (long)start_pos + T, cache_cap);
+        if ((long)start_pos + T > m->cfg.max_positions)
+            return fail(LLB_E_CAPACITY, "start_pos+T=%ld exceeds max_positions=%d", (long)start_pos + T,
+                        m->cfg.max_positions);
+    }
+    const bool lo = last_only != 0;
+    const ModelWs p = plan_model_ws(m, B, T, lo);
+    if (ws_bytes < p.total) return fail(LLB_E_INVALID, "workspace too small: %zu < %zu bytes", ws_bytes, p.total);
+    hipStream_t s = (hipStream_t)stream;
+    char* w = (char*)ws;
+    float* x = (float*)(w + p.x);
+    const int d = m->cfg.d_model, M = B * T;
+    hipError_t e = llb::embed_launch(tokens, m->embed, x, M, d, m->vocab, s);
+    if (e != hipSuccess) return hip_fail(e, "embedding");
+    for (int l = 0; l < m->n_layers; ++l) {
+        const llb_status st =
+            T == 1 ? llb_block_decode(m->layers[l], x, x, B, start_pos, k_caches[l], v_caches[l], cache_cap,
+                                      w + p.blk, p.blk_bytes, stream)
+                   : llb_block_prefill_at(m->layers[l], x, x, B, T, start_pos, k_caches[l], v_caches[l],
+                                          cache_cap, w + p.blk, p.blk_bytes, stream);
+        if (st != LLB_OK) return st;
+    }
+    const float* src = x;
+    int R = M;
+    if (lo && T > 1) {
+        e = llb::last_rows_launch(x, (float*)(w + p.xl), B, T, d, s);
+        if (e != hipSuccess) return hip_fail(e, "last rows");
+        src = (const float*)(w + p.xl);
+        R = B;
+    }
+    // final RMSNorm operand (bf16 x * g and fp32 sum of squares), then the head
+    // with the row's 1/rms in its epilogue
+    void* a = w + p.a;
+    float* ssq = (float*)(w + p.ssq);
+    e = llb::norm_rows_launch(src, m->gain, a, ssq, R, d, s);
+    if (e != hipSuccess) return hip_fail(e, "final RMSNorm");
+    llb::GemmArgs g{};
+    g.A = a; g.W = m->head; g.M = R; g.N = m->vocab; g.K = d; g.eps = m->cfg.eps;
+    g.ssq_in = ssq; g.ssq_count = 1;
+    g.epi.kind = llb::EPI_LOGITS; g.epi.out = logits;
+    if (R <= 64) {
+        e = llb::gemv_bf16_launch(g, llb::gemv_bf16_splits(R, m->vocab, d), (float*)(w + p.scratch), s);
+    } else {
+        const int tile = pick_tile(R, m->vocab, d, llb::EPI_LOGITS);
+        if (!llb::gemm_bf16_supports(tile, m->vocab, d, llb::EPI_LOGITS))
+            return fail(LLB_E_UNSUPPORTED, "LM head: no tile fits vocab=%d", m->vocab);
+        e = llb::gemm_bf16_launch(g, tile, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "LM head");
     return LLB_OK;
 }
 

@@ -117,6 +117,13 @@ LLB_DEV void epi_qkv8(const Epilogue& e, int m, int n, float* v) {
     *(uint4*)dst = pack8(v);
 }
 
+// out = C (fp32 logits, two 16-byte stores).
+LLB_DEV void epi_store8(const Epilogue& e, int m, int n, int N, const float* v) {
+    const size_t idx = (size_t)m * N + n;
+    *(float4*)(e.out + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(e.out + idx + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 // h = resid + C (fp32, two 16-byte loads and stores); returns h in v.
 LLB_DEV void epi_resid8(const Epilogue& e, int m, int n, int N, float* v) {
     const size_t idx = (size_t)m * N + n;

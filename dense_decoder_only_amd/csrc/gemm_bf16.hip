@@ -149,7 +149,7 @@ gemm_bf16_kernel(GemmArgs args) {
     };
 
     static_assert(BM <= 64 * NW, "one thread per tile row");
-    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
     const int nk = K / BK;
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
@@ -414,6 +414,8 @@ gemm_bf16_kernel(GemmArgs args) {
                 *(float4*)&v[4] = *(const float4*)&stile[row * SROW + ch * 8 + 4];
                 if constexpr (EPI == EPI_QKV) {
                     if (m < M) epi_qkv8(e, m, n, v);
+                } else if constexpr (EPI == EPI_LOGITS) {
+                    if (m < M) epi_store8(e, m, n, N, v);
                 } else {
                     float ss = 0.f;
                     if (m < M) {
@@ -554,6 +556,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
         case EPI_SWIGLU: return launch_one<BM, BN, WM, WN, BK, ST, OCC, SCHED, EPI_SWIGLU>(a, s);
         case EPI_RESID: return launch_one<BM, BN, WM, WN, BK, ST, OCC, SCHED, EPI_RESID>(a, s);
         case EPI_RESID_NORM: return launch_one<BM, BN, WM, WN, BK, ST, OCC, SCHED, EPI_RESID_NORM>(a, s);
+        case EPI_LOGITS: return launch_one<BM, BN, WM, WN, BK, ST, OCC, SCHED, EPI_LOGITS>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

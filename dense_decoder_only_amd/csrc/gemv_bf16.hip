@@ -96,7 +96,7 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
 
     // row scale of the normalised-operand epilogues, loaded before the copies
     // start (its loads are retired before the first wait on them)
-    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
     float my_scale = 1.0f;
     if (SCALED && tid < M) my_scale = row_scale(args, tid);
 
@@ -188,6 +188,11 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
             const int m = idx / GV_BN, c = idx % GV_BN;
             epi_resid(e, m, n0 + c, N, sred[idx]);
         }
+    } else if constexpr (EPI == EPI_LOGITS) {
+        for (int idx = tid; idx < M * GV_BN; idx += 256) {
+            const int m = idx / GV_BN, c = idx % GV_BN;
+            e.out[(size_t)m * N + n0 + c] = sred[idx] * sscale[m];
+        }
     } else if constexpr (EPI == EPI_SWIGLU) {
         // 128 columns = two groups [gate 32 | up 32]: 64 features per row
         for (int idx = tid; idx < M * 64; idx += 256) {
@@ -215,7 +220,7 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
 template <int EPI>
 __global__ void __launch_bounds__(256)
 gemv_reduce_kernel(GemmArgs args, int splits, const float* __restrict__ part) {
-    constexpr int RPW = (EPI == EPI_RESID || EPI == EPI_RESID_NORM) ? 2 : 4;
+    constexpr int RPW = (EPI == EPI_RESID || EPI == EPI_RESID_NORM || EPI == EPI_LOGITS) ? 2 : 4;
     constexpr int TPR = 256 / RPW;
     const int M = args.M, N = args.N;
     const int MT = M <= 32 ? 32 : 64;
@@ -246,6 +251,8 @@ gemv_reduce_kernel(GemmArgs args, int splits, const float* __restrict__ part) {
         if (j == 0 && m < M) e.ssq_out[(size_t)tile * M + m] = s_ss[2 * (wave >> 1)] + s_ss[2 * (wave >> 1) + 1];
     } else if constexpr (EPI == EPI_RESID) {
         if (m < M) epi_resid(e, m, n0 + j, N, col(j));
+    } else if constexpr (EPI == EPI_LOGITS) {
+        if (m < M) e.out[(size_t)m * N + n0 + j] = col(j) * row_scale(args, m);
     } else if constexpr (EPI == EPI_SWIGLU) {
         if (m < M) {
             const int cg = (j >> 5) * 64 + (j & 31);
@@ -272,7 +279,7 @@ hipError_t launch_epi(const GemmArgs& a, int splits, float* part, hipStream_t s)
         hipLaunchKernelGGL((gemv_bf16_kernel<2, EPI>), grid, dim3(256), 0, s, a, splits, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    constexpr int RPW = (EPI == EPI_RESID || EPI == EPI_RESID_NORM) ? 2 : 4;
+    constexpr int RPW = (EPI == EPI_RESID || EPI == EPI_RESID_NORM || EPI == EPI_LOGITS) ? 2 : 4;
     const dim3 rgrid((a.N / GV_BN) * ((a.M + RPW - 1) / RPW));
     hipLaunchKernelGGL((gemv_reduce_kernel<EPI>), rgrid, dim3(256), 0, s, a, splits, part);
     return hipGetLastError();
@@ -310,6 +317,7 @@ hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_
         case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, splits, ws, s);
         case EPI_RESID: return launch_epi<EPI_RESID>(a, splits, ws, s);
         case EPI_RESID_NORM: return launch_epi<EPI_RESID_NORM>(a, splits, ws, s);
+        case EPI_LOGITS: return launch_epi<EPI_LOGITS>(a, splits, ws, s);
         default: return hipErrorInvalidValue;
     }
 }

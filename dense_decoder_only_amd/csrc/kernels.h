@@ -7,7 +7,7 @@
 
 namespace llb {
 
-enum EpiKind : int { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_RESID_NORM = 3 };
+enum EpiKind : int { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_RESID_NORM = 3, EPI_LOGITS = 4 };
 
 // What a projection does with its fp32 result C[m, n] (after the row's inverse
 // RMS is applied when the A operand was normalised).
@@ -36,6 +36,8 @@ struct Epilogue {
     // EPI_SWIGLU: columns come in 64-wide groups [gate 32 | up 32]; feature
     // f = group*32 + j gets u[m, f] = SiLU(C_gate) * C_up, u is [M, N/2].
     void* u_out;
+    // EPI_LOGITS: out[m, n] = C[m, n] (fp32 [M, N]; C carries the row's 1/rms
+    // like EPI_QKV and EPI_SWIGLU).  Uses `out`.
 };
 
 // C = A . W^T.  W: [N, K], fp32 row-major or bf16 in the tiled layout below.
@@ -111,6 +113,13 @@ hipError_t attn_decode_bf16_launch(const AttnArgs& a, float* ws, hipStream_t s);
 hipError_t attn_f32_launch(const AttnArgs& a, hipStream_t s);
 
 // ---- cache helpers ---------------------------------------------------------
+// ---- model: token embedding and the LM head's rows ---------------------------
+// x[m, :] = fp32(E[tok[m], :]) for the bf16 table E [vocab, d] (ids outside the
+// vocabulary give NaN rows); tok: device [M].
+hipError_t embed_launch(const int* tok, const void* E, float* x, int M, int d, int vocab, hipStream_t s);
+// dst[b, :] = src[b*T + T - 1, :], fp32 rows of d.
+hipError_t last_rows_launch(const float* src, float* dst, int B, int T, int d, hipStream_t s);
+
 // dst[0..n) = src[0..n) (src on the host), through kernel arguments: ordered on
 // stream s like the kernels, and src may be reused as soon as this returns.
 hipError_t store_ints_launch(int* dst, const int* src, int n, hipStream_t s);

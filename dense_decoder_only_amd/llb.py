@@ -33,6 +33,7 @@ EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes"
             "llb_block_prefill", "llb_block_prefill_at", "llb_block_decode", "llb_block_decode_ragged", "llb_kv_append", "llb_attention_prefill",
             "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
             "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles",
+            "llb_model_create", "llb_model_destroy", "llb_model_workspace_bytes", "llb_model_forward",
             "llb_last_error")
 
 STAGES = ("qkv", "attention", "o_proj", "gate_up", "down")
@@ -106,6 +107,16 @@ def load_library(path: str = LIB_PATH):
     lib.llb_gemm_tile_info.restype = ctypes.c_int
     lib.llb_block_set_tiles.argtypes = [vp, i32, i32, i32, i32]
     lib.llb_block_set_tiles.restype = ctypes.c_int
+    lib.llb_model_create.argtypes = [ctypes.POINTER(llb_config), i32, i32, vp, ctypes.POINTER(llb_weights), vp, vp,
+                                     vp, ctypes.POINTER(vp)]
+    lib.llb_model_create.restype = ctypes.c_int
+    lib.llb_model_destroy.argtypes = [vp]
+    lib.llb_model_destroy.restype = ctypes.c_int
+    lib.llb_model_workspace_bytes.argtypes = [vp, i32, i32, i32]
+    lib.llb_model_workspace_bytes.restype = sz
+    lib.llb_model_forward.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, vp,
+                                      vp, sz, vp]
+    lib.llb_model_forward.restype = ctypes.c_int
     lib.llb_last_error.argtypes = []
     lib.llb_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -233,6 +244,65 @@ def llb_attention_decode(blk: Block, q, k_cache, v_cache, o, B, start_pos, cache
                                                _ptr(o), B, start_pos, cache_cap, _ptr(ws),
                                                ws.numel() * ws.element_size(), _stream(stream)),
            "llb_attention_decode")
+
+
+class Model:
+    """A created model handle (llb_model*).  Destroy with llb_model_destroy."""
+
+    def __init__(self, handle: int, cfg: llb_config, n_layers: int, vocab: int):
+        self.handle = ctypes.c_void_p(handle)
+        self.cfg = cfg
+        self.n_layers = n_layers
+        self.vocab = vocab
+
+
+_BLOCK_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+def llb_model_create(cfg: llb_config, layers, vocab: int, embed: torch.Tensor, final_norm: torch.Tensor,
+                     lm_head: torch.Tensor, stream=None) -> Model:
+    """layers: a list of per-layer weight dicts (device tensors, as for llb_block_create)."""
+    for t in [embed, final_norm, lm_head] + [w[k] for w in layers for k in _BLOCK_KEYS]:
+        if not t.is_contiguous():
+            raise ValueError("model weights must be contiguous")
+    arr = (llb_weights * max(1, len(layers)))()
+    for i, w in enumerate(layers):
+        arr[i] = llb_weights(**{k: w[k].data_ptr() for k in _BLOCK_KEYS})
+    out = ctypes.c_void_p()
+    _check(load_library().llb_model_create(ctypes.byref(cfg), len(layers), vocab, _ptr(embed), arr, _ptr(final_norm),
+                                           _ptr(lm_head), _stream(stream), ctypes.byref(out)), "llb_model_create")
+    return Model(out.value, cfg, len(layers), vocab)
+
+
+def llb_model_destroy(m: Model) -> None:
+    _check(load_library().llb_model_destroy(m.handle), "llb_model_destroy")
+    m.handle = ctypes.c_void_p(0)
+
+
+def llb_model_workspace_bytes(m: Model, B: int, T: int, last_only: bool) -> int:
+    return int(load_library().llb_model_workspace_bytes(m.handle, B, T, 1 if last_only else 0))
+
+
+def model_workspace(m: Model, B: int, T: int, last_only: bool, device="cuda") -> torch.Tensor:
+    n = llb_model_workspace_bytes(m, B, T, last_only)
+    if n == 0:
+        raise ValueError("llb_model_workspace_bytes returned 0 (bad handle or sizes)")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def llb_model_forward(m: Model, tokens, B, T, start_pos, k_caches, v_caches, cache_cap, last_only, logits, ws,
+                      stream=None):
+    """tokens: int32 device tensor [B, T]; k_caches / v_caches: lists of n_layers device tensors."""
+    if tokens.dtype != torch.int32:
+        raise ValueError("tokens must be int32")
+    if len(k_caches) != m.n_layers or len(v_caches) != m.n_layers:
+        raise ValueError("one K and one V cache per layer")
+    n = max(1, m.n_layers)
+    kc = (ctypes.c_void_p * n)(*[c.data_ptr() for c in k_caches])
+    vc = (ctypes.c_void_p * n)(*[c.data_ptr() for c in v_caches])
+    _check(load_library().llb_model_forward(m.handle, _ptr(tokens), B, T, start_pos, kc, vc, cache_cap,
+                                            1 if last_only else 0, _ptr(logits), _ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(stream)), "llb_model_forward")
 
 
 def llb_gemm_num_tiles() -> int:

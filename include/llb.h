@@ -194,6 +194,39 @@ size_t llb_attention_workspace_bytes(const llb_block* blk, int32_t B, int32_t n_
 llb_status llb_block_set_stage_timing(llb_block* blk, int32_t enable);
 llb_status llb_block_stage_times(llb_block* blk, float* ms, int32_t* n_calls);
 
+/* ---- Model: embedding, n_layers blocks, final RMSNorm, LM head ------------
+ * "Llama 3.1 70B" (sections on the token embedding, the stack of transformer
+ * layers and the LM head) and "How Llama 3.1 Generates the Next Token" (the
+ * unembedding: a final RMSNorm, then one linear map from d_model to the
+ * vocabulary, untied from the embedding).  bf16 weights only.
+ *
+ * llb_model_create: cfg as for llb_block_create (every layer has that shape);
+ *   embed and lm_head are [vocab, d_model] bf16 device matrices, final_norm [d]
+ *   bf16, layers an array of n_layers weight sets.  Everything is copied (the
+ *   caller may free its tensors afterwards).  vocab must be a multiple of 128
+ *   (LLB_E_UNSUPPORTED otherwise).  Uses the current device; synchronises.
+ * llb_model_forward: tokens [B, T] int32 device ids at positions
+ *   start_pos..start_pos+T-1 of every sequence; k_caches / v_caches are HOST
+ *   arrays of n_layers device pointers, each a cache as in llb_block_prefill.
+ *   T = 1 decodes (one token at position start_pos, reading L = start_pos + 1
+ *   keys per layer), T > 1 prefills a chunk.  logits: fp32, [B, T, vocab], or
+ *   [B, vocab] for the last position of each sequence when last_only != 0.  An
+ *   id outside [0, vocab) gives NaN hidden states and logits to its sequence
+ *   (through attention the NaN reaches the sequence's other positions of this
+ *   call and the cache rows it writes), never to other sequences; the table is
+ *   never read out of range.  Needs start_pos + T <= cache_cap and
+ *   <= max_positions; the workspace is llb_model_workspace_bytes(m, B, T,
+ *   last_only) bytes.  Enqueues on `stream`. */
+typedef struct llb_model llb_model;
+llb_status llb_model_create(const llb_config* cfg, int32_t n_layers, int32_t vocab, const void* embed,
+                            const llb_weights* layers, const void* final_norm, const void* lm_head,
+                            void* stream, llb_model** out);
+llb_status llb_model_destroy(llb_model* m);
+size_t llb_model_workspace_bytes(const llb_model* m, int32_t B, int32_t T, int32_t last_only);
+llb_status llb_model_forward(llb_model* m, const int32_t* tokens, int32_t B, int32_t T, int32_t start_pos,
+                             void* const* k_caches, void* const* v_caches, int32_t cache_cap,
+                             int32_t last_only, float* logits, void* ws, size_t ws_bytes, void* stream);
+
 /* Tuning and test hooks for the bf16 prefill projections.  The library holds
  * a fixed table of GEMM tile configurations (workgroup tile BM x BN, waves,
  * k-depth, pipeline stages, schedule); by default each projection picks one

@@ -18,3 +18,4 @@ from .block import (  # noqa: F401
     swiglu,
     to64,
 )
+from .model import embed, model_forward, model_param_counts  # noqa: F401,E402

@@ -1,0 +1,183 @@
+"""GPU parity of the model forward (embedding, L blocks, final RMSNorm, LM head)
+against the fp64 oracle, through the C ABI.
+
+Bar on the logits: max|gpu - oracle| / rms(oracle) <= 2e-2 * sqrt(L + 1).  Each
+block's output carries the single-block bf16 error (<= 2e-2 by the same metric,
+the block's bar) into the fp32 trunk; independent per-block errors add in
+quadrature over the L blocks, and the head's bf16 operand adds one more term.
+Layer 0's new cache rows keep the block bar (its input, the embedding, is exact).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import bf16_err, note, rel_err, upload_weights
+
+pytestmark = pytest.mark.gpu
+
+SMALL = workloads.BlockShape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+
+
+def _bar(L):
+    return 2e-2 * math.sqrt(L + 1)
+
+
+class GpuModel:
+    def __init__(self, shp, params, cap):
+        from dense_decoder_only_amd import llb
+        self.llb = llb
+        self.shape = shp
+        self.cfg = llb.make_config(shp, cap)
+        dev = [upload_weights(w) for w in params["layers"]]
+        self.m = llb.llb_model_create(self.cfg, dev, params["embed"].shape[0], params["embed"].cuda(),
+                                      params["final_norm"].cuda(), params["lm_head"].cuda())
+        del dev
+
+    def forward(self, tokens, start_pos, kcs, vcs, last_only):
+        B, T = tokens.shape
+        V = self.m.vocab
+        logits = torch.empty((B, V) if last_only else (B, T, V), dtype=torch.float32, device="cuda")
+        ws = self.llb.model_workspace(self.m, B, T, last_only)
+        self.llb.llb_model_forward(self.m, tokens.cuda().contiguous(), B, T, start_pos, kcs, vcs, kcs[0].shape[2]
+                                   if kcs else 1, last_only, logits, ws)
+        torch.cuda.synchronize()
+        return logits.cpu()
+
+    def close(self):
+        self.llb.llb_model_destroy(self.m)
+
+
+def _caches(shp, L, B, P, cap, gen):
+    kc, vc = [], []
+    for _ in range(L):
+        k, v = workloads.make_cache(shp, B, P, cap, gen)
+        kc.append(k)
+        vc.append(v)
+    return kc, vc
+
+
+@pytest.mark.parametrize("L,B,T,last_only", [(3, 2, 100, False), (3, 2, 100, True), (1, 1, 300, True),
+                                             (2, 3, 37, False)])
+def test_model_prefill(L, B, T, last_only):
+    V = 1024
+    params, gen = workloads.make_model_weights(SMALL, L, V, 40 + L + T)
+    tok = workloads.make_tokens(B, T, V, gen)
+    cap = workloads.cache_capacity(T)
+    kc, vc = _caches(SMALL, L, B, 0, cap, gen)
+    note(f"model prefill L={L} B={B} T={T} last_only={last_only}")
+    gm = GpuModel(SMALL, params, cap)
+    try:
+        kd, vd = [k.cuda() for k in kc], [v.cuda() for v in vc]
+        logits = gm.forward(tok, 0, kd, vd, last_only)
+    finally:
+        gm.close()
+    ref, ks, vs = oracle.model_forward(SMALL, params, tok, kc, vc, 0, last_only=last_only)
+    e = rel_err(logits, ref)
+    e_k = bf16_err(kd[0].cpu()[:, :, :T], ks[0])
+    note(f"  logits {e:.2e} (bar {_bar(L):.2e})  layer-0 k {e_k:.3f}")
+    assert e <= _bar(L) and e_k <= 1.0
+    assert torch.isfinite(logits).all()
+
+
+def test_model_decode_and_chunks_continue_a_prefill():
+    """GPU prefill of T1 tokens, a GPU chunk of T2, then GPU decode of one token:
+    each against the oracle's single forward over all T1 + T2 + 1 tokens."""
+    L, B, T1, T2, V = 3, 2, 64, 40, 1024
+    params, gen = workloads.make_model_weights(SMALL, L, V, 91)
+    tok = workloads.make_tokens(B, T1 + T2 + 1, V, gen)
+    cap = workloads.cache_capacity(T1 + T2 + 1)
+    kc, vc = _caches(SMALL, L, B, 0, cap, gen)
+    gm = GpuModel(SMALL, params, cap)
+    try:
+        kd, vd = [k.cuda() for k in kc], [v.cuda() for v in vc]
+        gm.forward(tok[:, :T1], 0, kd, vd, True)
+        chunk = gm.forward(tok[:, T1:T1 + T2], T1, kd, vd, False)
+        step = gm.forward(tok[:, T1 + T2:], T1 + T2, kd, vd, True)
+    finally:
+        gm.close()
+    ref, _, _ = oracle.model_forward(SMALL, params, tok, kc, vc, 0)
+    e_c = rel_err(chunk, ref[:, T1:T1 + T2])
+    e_d = rel_err(step, ref[:, T1 + T2])
+    note(f"model continuation: chunk {e_c:.2e}  decode {e_d:.2e}  (bar {_bar(L):.2e})")
+    assert e_c <= _bar(L) and e_d <= _bar(L)
+
+
+def test_model_out_of_vocabulary_token_stays_in_its_sequence():
+    """An id outside the vocabulary turns its sequence's hidden states NaN (they
+    reach the sequence's other positions through attention: a masked weight of 0
+    times a NaN value is NaN) and leaves the other sequences exact."""
+    L, B, T, V = 2, 2, 20, 1024
+    params, gen = workloads.make_model_weights(SMALL, L, V, 5)
+    tok = workloads.make_tokens(B, T, V, gen)
+    tok[1, 7] = V                       # outside the vocabulary
+    cap = workloads.cache_capacity(T)
+    kc, vc = _caches(SMALL, L, B, 0, cap, gen)
+    gm = GpuModel(SMALL, params, cap)
+    try:
+        logits = gm.forward(tok, 0, [k.cuda() for k in kc], [v.cuda() for v in vc], False)
+    finally:
+        gm.close()
+    assert torch.isfinite(logits[0]).all()
+    assert torch.isnan(logits[1, 7:]).all()
+    ref, _, _ = oracle.model_forward(SMALL, params, tok[:1], [k[:1] for k in kc], [v[:1] for v in vc], 0)
+    assert rel_err(logits[:1], ref) <= _bar(L)
+
+
+def test_model_rejects_bad_calls():
+    from dense_decoder_only_amd import llb
+    L, V, cap = 2, 1024, 64
+    params, gen = workloads.make_model_weights(SMALL, L, V, 6)
+    gm = GpuModel(SMALL, params, cap)
+    try:
+        tok = workloads.make_tokens(1, 8, V, gen).cuda()
+        kc, vc = _caches(SMALL, L, 1, 0, cap, gen)
+        kd, vd = [k.cuda() for k in kc], [v.cuda() for v in vc]
+        logits = torch.empty(1, V, device="cuda")
+        ws = llb.model_workspace(gm.m, 1, 8, True)
+        with pytest.raises(llb.LlbError) as ei:          # start_pos + T > cache_cap
+            llb.llb_model_forward(gm.m, tok, 1, 8, cap - 4, kd, vd, cap, True, logits, ws)
+        assert ei.value.status == llb.LLB_E_CAPACITY
+        with pytest.raises(ValueError):                  # one cache per layer
+            llb.llb_model_forward(gm.m, tok, 1, 8, 0, kd[:1], vd[:1], cap, True, logits, ws)
+        with pytest.raises(llb.LlbError) as ei:          # workspace too small
+            llb.llb_model_forward(gm.m, tok, 1, 8, 0, kd, vd, cap, True, logits, ws[:16])
+        assert ei.value.status == llb.LLB_E_INVALID
+    finally:
+        gm.close()
+    with pytest.raises(llb.LlbError) as ei:              # vocabulary not a multiple of 128
+        llb.llb_model_create(llb.make_config(SMALL, 64), [], 1000, params["embed"][:1000].cuda(),
+                             params["final_norm"].cuda(), params["lm_head"][:1000].cuda())
+    assert ei.value.status == llb.LLB_E_UNSUPPORTED
+
+
+def test_model_full_width_8b_layers():
+    """Llama-3.1-8B widths (d 4096, 32/8 heads, d_ff 14336, vocab 128256) with two
+    layers: decode of 4 sequences at P = 64 over random caches (logits of every
+    vocabulary entry) and a 512-token prefill's last-position logits."""
+    shp = workloads.LLAMA31_8B
+    L, V = 2, 128256
+    params, gen = workloads.make_model_weights(shp, L, V, 77)
+    gm = GpuModel(shp, params, 1024)
+    try:
+        B, P = 4, 64
+        tok = workloads.make_tokens(B, 1, V, gen)
+        kc, vc = _caches(shp, L, B, P, 1024, gen)
+        note("model full width: GPU decode")
+        dec = gm.forward(tok, P, [k.cuda() for k in kc], [v.cuda() for v in vc], True)
+        T = 512
+        tok2 = workloads.make_tokens(1, T, V, gen)
+        kc2, vc2 = _caches(shp, L, 1, 0, 1024, gen)
+        note("model full width: GPU prefill")
+        pre = gm.forward(tok2, 0, [k.cuda() for k in kc2], [v.cuda() for v in vc2], True)
+    finally:
+        gm.close()
+    note("model full width: oracle")
+    ref_d, _, _ = oracle.model_forward(shp, params, tok, kc, vc, P, last_only=True)
+    ref_p, _, _ = oracle.model_forward(shp, params, tok2, kc2, vc2, 0, last_only=True)
+    e_d, e_p = rel_err(dec, ref_d), rel_err(pre, ref_p)
+    note(f"  decode {e_d:.2e}  prefill {e_p:.2e}  (bar {_bar(L):.2e})")
+    assert e_d <= _bar(L) and e_p <= _bar(L)

@@ -165,6 +165,26 @@ def make_weights(shape: BlockShape, seed: int, device="cpu", gen: Optional[torch
     return w, gen
 
 
+def make_model_weights(shape: BlockShape, n_layers: int, vocab: int, seed: int, device="cpu"):
+    """A model's weights: the embedding table [vocab, d] ~ N(0, 1) (the trunk then
+    starts at unit RMS, like the block inputs), n_layers block weight sets
+    (make_weights, drawn in layer order), the final gain 1 + N(0, 0.1) and the LM
+    head [vocab, d] ~ N(0, 1/d).  Returns (params, generator)."""
+    gen = _gen(seed, device)
+    wd = shape.torch_dtype()
+    d = shape.d_model
+    params = {"embed": _randn((vocab, d), gen, device, out_dtype=wd)}
+    params["layers"] = [make_weights(shape, seed, device, gen=gen)[0] for _ in range(n_layers)]
+    params["final_norm"] = _randn((d,), gen, device, std=0.1 ** 0.5, mean=1.0, out_dtype=wd)
+    params["lm_head"] = _randn((vocab, d), gen, device, std=d ** -0.5, out_dtype=wd)
+    return params, gen
+
+
+def make_tokens(B: int, T: int, vocab: int, gen: torch.Generator, device="cpu") -> torch.Tensor:
+    """Token ids, uniform over the vocabulary, int32 [B, T]."""
+    return torch.randint(0, vocab, (B, T), generator=gen, device=device, dtype=torch.int64).to(torch.int32)
+
+
 def make_x(B: int, T: int, d: int, gen: torch.Generator, device="cpu") -> torch.Tensor:
     """Residual-stream input x ~ N(0, 1), fp32, [B, T, d]."""
     return _randn((B, T, d), gen, device)
