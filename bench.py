@@ -17,6 +17,9 @@ reports:
     each timed the same way (decode with two weight and
     cache sets used alternately so that the 256 MB last-level cache cannot hold
     the working set between steps), with per-stage times.
+  * model_workloads: the whole Llama-3.1-8B model (embedding, 32 blocks, final
+    RMSNorm, LM head over 128256 ids) on 32-sequence decode (P=1000) and on a
+    2048-token prefill (last-position logits).
 Inputs are seeded synthetic tensors with the workload's shapes and
 distributions; nothing is read from disk.
 """
@@ -158,6 +161,63 @@ def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
     torch.cuda.empty_cache()
     per_call = {k: v / calls for k, v in stage_ms.items()}
     return wl, total_ms / steps, per_call
+
+
+def time_model(name, steps, warmup, warm_seconds=0.5):
+    """Times one whole-model forward per step (embedding, every block, final norm,
+    LM head; last-position logits for a prefill).  Returns (workload, ms/step,
+    algorithmic bytes, algorithmic FLOPs)."""
+    import torch
+    import workloads
+    from dense_decoder_only_amd import llb
+
+    wl = workloads.get(name)
+    shp = wl.shape
+    cap = workloads.cache_capacity(wl.P + wl.T)
+    log(f"{name}: building the {wl.layers}-layer model on the GPU")
+    params, gen = workloads.make_model_weights(shp, wl.layers, wl.vocab, wl.seed, device="cuda")
+    model = llb.llb_model_create(llb.make_config(shp, cap), params["layers"], wl.vocab, params["embed"],
+                                 params["final_norm"], params["lm_head"])
+    del params
+    torch.cuda.empty_cache()
+    kcs, vcs = [], []
+    for _ in range(wl.layers):
+        k, v = workloads.make_cache(shp, wl.B, wl.P, cap, gen, device="cuda")
+        kcs.append(k)
+        vcs.append(v)
+    tok = workloads.make_tokens(wl.B, wl.T, wl.vocab, gen, device="cuda")
+    last_only = wl.mode == "prefill"
+    logits = torch.empty((wl.B, wl.vocab), dtype=torch.float32, device="cuda")
+    ws = llb.model_workspace(model, wl.B, wl.T, last_only)
+
+    def step():
+        llb.llb_model_forward(model, tok, wl.B, wl.T, wl.P, kcs, vcs, cap, last_only, logits, ws)
+
+    t_warm = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - t_warm < warm_seconds:
+        step()
+        n_warm += 1
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    llb.llb_model_destroy(model)
+    del kcs, vcs, ws, logits
+    torch.cuda.empty_cache()
+    by = stage_bytes(wl)
+    fl = stage_flops(wl)
+    es = 2
+    head_rows = wl.B
+    total_bytes = wl.layers * sum(by.values()) + wl.vocab * shp.d_model * es + head_rows * wl.vocab * 4
+    total_flops = wl.layers * sum(fl.values()) + 2 * head_rows * wl.vocab * shp.d_model
+    return wl, ms, total_bytes, total_flops
 
 
 def summarize(wl, ms, stage_ms):
@@ -314,6 +374,23 @@ def main():
             others[other] = summarize(owl, oms, ost)
             log(f"{other}: {oms:.3f} ms/step")
         result["other_workloads"] = others
+
+    if not args.no_others and args.only is None:
+        models = {}
+        for mname in ("8b_bf16_model_decode", "8b_bf16_model_prefill"):
+            mwl, mms, mby, mfl = time_model(mname, 10, 2, warm_seconds=args.warmup_seconds)
+            tok = mwl.B * mwl.T
+            entry = {"tokens_per_s": tok / (mms * 1e-3), "ms_per_step": mms, "layers": mwl.layers,
+                     "vocab": mwl.vocab}
+            if mwl.mode == "decode":
+                entry["hbm_gbs"] = mby / (mms * 1e-3) / 1e9
+                entry["frac_hbm_peak"] = entry["hbm_gbs"] / PEAK_HBM_GBS
+            else:
+                entry["tflops"] = mfl / (mms * 1e-3) / 1e12
+                entry["frac_bf16_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
+            models[mname] = entry
+            log(f"{mname}: {mms:.3f} ms/step")
+        result["model_workloads"] = models
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(name)

@@ -92,6 +92,8 @@ class Workload:
     P: int = 0         # cached positions before the call (start position)
     seed: int = 0
     ragged: bool = False  # decode: sequence b starts at ragged_positions(self)[b] (mean P)
+    layers: int = 0       # > 0: a whole model of this many blocks with embedding and LM head
+    vocab: int = 0
 
     @property
     def tokens(self) -> int:
@@ -109,6 +111,12 @@ CONFIGS: Dict[str, Workload] = {
     "8b_bf16_decode": Workload("8b_bf16_decode", LLAMA31_8B, "decode", B=32, T=1, P=1000, seed=3),
     "70b_bf16_decode": Workload("70b_bf16_decode", LLAMA31_70B, "decode", B=64, T=1, P=4096, seed=4),
     "70b_bf16_prefill": Workload("70b_bf16_prefill", LLAMA31_70B, "prefill", B=1, T=16384, seed=5),
+    # the whole Llama-3.1-8B stack: embedding, 32 blocks, final norm, LM head over
+    # 128256 ids (logits of the last position for the prefill)
+    "8b_bf16_model_decode": Workload("8b_bf16_model_decode", LLAMA31_8B, "decode", B=32, T=1, P=1000, seed=8,
+                                     layers=32, vocab=128256),
+    "8b_bf16_model_prefill": Workload("8b_bf16_model_prefill", LLAMA31_8B, "prefill", B=1, T=2048, seed=9,
+                                      layers=32, vocab=128256),
     # 32 sequences of different lengths, evenly spread over 0..2P (mean P = 1000)
     "8b_bf16_ragged_decode": Workload("8b_bf16_ragged_decode", LLAMA31_8B, "decode", B=32, T=1, P=1000,
                                       seed=7, ragged=True),
