@@ -147,12 +147,15 @@ __device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, in
             float v[8];
             unpack_bf16x8(vf[i], v);
             const int kl = ps * KPL + i;
+            // the G weights of key kl, read as whole float4 rows of sP
+            float p[G < 4 ? 4 : G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = sP[kl][h];
+            for (int h4 = 0; h4 < (G + 3) / 4; ++h4)
+                *(float4*)&p[4 * h4] = *(const float4*)&sP[kl][4 * h4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[h][e] += p * v[e];
-            }
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[h][e] += p[h] * v[e];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -193,7 +196,7 @@ __global__ void __launch_bounds__(256)
 attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part_o,
                    float* __restrict__ part_ml) {
     constexpr int NC = HD / 8;
-    __shared__ float sP[4][16][16];     // per wave: p[key][head]
+    __shared__ __attribute__((aligned(16))) float sP[4][16][16];     // per wave: p[key][head]
     __shared__ float sAl[4][16];        // per wave: alpha[head]
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -234,7 +237,7 @@ template <int HD, int G>
 __global__ void __launch_bounds__(64 * AD_FW)
 attn_decode_fused_kernel(AttnArgs a) {
     constexpr int NC = HD / 8;
-    __shared__ float sP[AD_FW][16][16];
+    __shared__ __attribute__((aligned(16))) float sP[AD_FW][16][16];
     __shared__ float sAl[AD_FW][16];
     __shared__ float sO[AD_FW][G][HD];
     __shared__ float sM[AD_FW][G], sL[AD_FW][G];
