@@ -427,6 +427,36 @@ def test_bf16_prefill_is_deterministic():
         gb.close()
 
 
+def test_bf16_decode_split_k_with_dirty_workspace():
+    """The decode projections split K over workgroups and sum the partials in
+    split order through the workspace.  A workspace full of stale bytes, and
+    calls back to back on one workspace, give bit-identical results to a
+    zeroed one."""
+    shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+    B, P = 7, 77
+    cap = workloads.cache_capacity(P + 1)
+    w, x, kc, vc = gen_inputs(shp, 17, B, 1, P, cap)
+    note("decode split-K counters")
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        from dense_decoder_only_amd import llb
+        ws = gb.workspace(B, 1)
+        outs = []
+        for fill in (0, 0xFF, 0x01, None, None):
+            if fill is not None:
+                ws.fill_(fill)
+            kd, vd = kc.cuda(), vc.cuda()
+            y = torch.empty(B, 1, shp.d_model, device="cuda")
+            llb.llb_block_decode(gb.blk, x.cuda(), y, B, P, kd, vd, cap, ws)
+            outs.append((y.cpu(), kd.cpu()))
+        for y, k in outs[1:]:
+            assert torch.equal(y, outs[0][0]) and torch.equal(k, outs[0][1])
+        y_ref, _, _ = oracle.block_forward(shp, w, x, kc, vc, P)
+        assert rel_err(outs[0][0], y_ref) <= 2e-2
+    finally:
+        gb.close()
+
+
 def test_y_may_alias_x():
     shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
     B, T = 1, 40
