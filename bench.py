@@ -134,19 +134,27 @@ def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     log(f"{name}: {n_warm} warm-up steps")
-    for b in blocks:
-        llb.llb_block_set_stage_timing(b, True)
-        llb.llb_block_stage_times(b)           # clear
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+
+    def timed_loop():
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    # The whole-call time comes from a loop without the per-stage events (each
+    # event record adds a few microseconds between kernels); a second loop with
+    # them gives the per-stage split.
+    total_ms = timed_loop()
+    for b in blocks:
+        llb.llb_block_set_stage_timing(b, True)
+        llb.llb_block_stage_times(b)           # clear
+    timed_loop()
     stage_ms = {k: 0.0 for k in llb.STAGES}
     calls = 0
     for b in blocks:
