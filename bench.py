@@ -86,7 +86,7 @@ def stage_bytes(wl):
 
 
 # ------------------------------------------------------------- GPU timing
-def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
+def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None, decode_rows=None):
     import torch
     import workloads
     from dense_decoder_only_amd import llb
@@ -103,6 +103,8 @@ def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None):
         blocks.append(llb.llb_block_create(llb.make_config(shp, cap), w))
         if tiles is not None:
             llb.llb_block_set_tiles(blocks[-1], *tiles)
+        if decode_rows is not None:
+            llb.llb_block_set_decode_rows(blocks[-1], *decode_rows)
         kc, vc = workloads.make_cache(shp, wl.B, workloads.max_start(wl), cap, gen, device=dev)
         caches.append((kc, vc))
     del w
@@ -300,6 +302,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--only", default=None, help="time only this workload (diagnostics)")
+    ap.add_argument("--decode-rows", default=None, metavar="Q,O,D",
+                    help="decode kernel of the QKV, O and down projections (-1 automatic, 0 split-K, "
+                         "16/32 narrow rows); with --only")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the "
                          "HBM byte counters FETCH_SIZE / WRITE_SIZE against a known size)")
@@ -324,7 +329,9 @@ def main():
         return
 
     name = args.only or HEADLINE
-    wl, ms, st = time_workload(name, args.steps, args.warmup, warm_seconds=args.warmup_seconds)
+    drows = tuple(int(v) for v in args.decode_rows.split(",")) if args.decode_rows else None
+    wl, ms, st = time_workload(name, args.steps, args.warmup, sets=2 if "decode" in name else 1,
+                               warm_seconds=args.warmup_seconds, decode_rows=drows)
     head = summarize(wl, ms, st)
     log(f"{name}: {ms:.3f} ms/step, {head['tokens_per_s']:.0f} tok/s")
 

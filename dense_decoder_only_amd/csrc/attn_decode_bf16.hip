@@ -60,15 +60,18 @@ __device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, in
     const int bg = b * a.n_kv + g;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
 
-    // Q fragments: B operand (column = head lane&15, dims 32kk + 8*(lane>>4) ..+8)
+    // Q fragments: B operand (column = head lane&15, dims 32kk + 8*(lane>>4) ..+8).
+    // Every load below is unconditional (indices clamped into range, unused
+    // values zeroed or masked afterwards): a load under a per-lane condition
+    // becomes a branch, across which the compiler can only wait for all loads
+    // in flight, which would serialise the prefetch.
     const int hq = lane & 15;
     bf16x8 qf[KST];
+    uint4 qv[KST];
     {
-        const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)b * a.n_heads + g * G + hq) * HD;
+        const bf16_t* qrow = (const bf16_t*)a.q + ((size_t)b * a.n_heads + g * G + min(hq, G - 1)) * HD;
 #pragma unroll
-        for (int kk = 0; kk < KST; ++kk)
-            qf[kk] = as_bf16x8(hq < G ? *(const uint4*)(qrow + 32 * kk + 8 * (lane >> 4))
-                                      : make_uint4(0, 0, 0, 0));
+        for (int kk = 0; kk < KST; ++kk) qv[kk] = *(const uint4*)(qrow + 32 * kk + 8 * (lane >> 4));
     }
 
     const size_t head_off = (size_t)bg * a.cap * HD;
@@ -84,19 +87,19 @@ __device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, in
     m_run = -INFINITY;
     l_run = 0.f;
 
-    // K and V of one 16-key step; the next step's loads are issued before the
-    // current step is computed (two register buffers)
+    // K and V of one 16-key step.  Keys at or past k_end read row k_end - 1
+    // instead (a row already fetched: no extra HBM traffic); their scores are
+    // masked to -inf, so their weights are 0 and their values add nothing.
+    const int last = max(k_end - 1, 0);
     auto load_step = [&](int kt, uint4 (&kf)[KST], uint4 (&vf)[KPL]) {
-        const int krow = kt + (lane & 15);
+        const int krow = min(kt + (lane & 15), last);
 #pragma unroll
         for (int kk = 0; kk < KST; ++kk)
-            kf[kk] = krow < k_end ? *(const uint4*)(Kg + (size_t)krow * HD + 32 * kk + 8 * (lane >> 4))
-                                  : make_uint4(0, 0, 0, 0);
+            kf[kk] = *(const uint4*)(Kg + (size_t)krow * HD + 32 * kk + 8 * (lane >> 4));
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
-            const int key = kt + ps * KPL + i;
-            vf[i] = key < k_end ? *(const uint4*)(Vg + (size_t)key * HD + 8 * pc)
-                                : make_uint4(0, 0, 0, 0);
+            const int key = min(kt + ps * KPL + i, last);
+            vf[i] = *(const uint4*)(Vg + (size_t)key * HD + 8 * pc);
         }
     };
     auto step = [&](int kt, const uint4 (&kf)[KST], const uint4 (&vf)[KPL]) {
@@ -162,20 +165,25 @@ __device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, in
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
     // DEPTH register buffers: the loads of the next DEPTH-1 steps are in flight
-    // while a step is computed
+    // while a step is computed.  The same loads are issued on every path (steps
+    // past the chunk re-read row k_end - 1), so the compiler's waits count
+    // exactly the DEPTH-1 younger steps.
     uint4 kf[DEPTH][KST], vf[DEPTH][KPL];
 #pragma unroll
-    for (int d = 0; d + 1 < DEPTH; ++d)
-        if (k_beg + 16 * d < k_end) load_step(k_beg + 16 * d, kf[d], vf[d]);
+    for (int d = 0; d + 1 < DEPTH; ++d) load_step(k_beg + 16 * d, kf[d], vf[d]);
+    // The query is consumed here, before the loop, so that no wait on it is
+    // left inside the loop (heads past the group are zero columns).
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+        asm volatile("" ::"v"(qv[kk].x), "v"(qv[kk].y), "v"(qv[kk].z), "v"(qv[kk].w));
+        qf[kk] = as_bf16x8(hq < G ? qv[kk] : make_uint4(0, 0, 0, 0));
+    }
     for (int kt = k_beg; kt < k_end; kt += 16 * DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int kc = kt + 16 * d;
-            if (kc < k_end) {
-                const int kn = kc + 16 * (DEPTH - 1);
-                if (kn < k_end) load_step(kn, kf[(d + DEPTH - 1) % DEPTH], vf[(d + DEPTH - 1) % DEPTH]);
-                step(kc, kf[d], vf[d]);
-            }
+            load_step(kc + 16 * (DEPTH - 1), kf[(d + DEPTH - 1) % DEPTH], vf[(d + DEPTH - 1) % DEPTH]);
+            if (kc < k_end) step(kc, kf[d], vf[d]);
         }
     }
 

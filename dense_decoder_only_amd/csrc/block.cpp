@@ -58,6 +58,7 @@ struct llb_block {
     float* g2;       // FFN RMSNorm gain, fp32 [d]
     float2* rope;    // [max_positions][hd/2] (cos, sin)
     int tile_qkv, tile_o, tile_gu, tile_down;  // bf16 prefill tile choice per projection (-1 = pick by M)
+    int dec_qkv, dec_o, dec_down;  // decode kernel per projection: -1 automatic, 0 split-K, 16/32 narrow rows
     int num_cus;                     // compute units of the device
     int timing;                      // record stage events on every call
     std::vector<hipEvent_t> events;  // 6 per recorded call
@@ -187,7 +188,9 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
         p.a1 = off; off += align_up(M * c.d_model * 2);
         p.a2 = off; off += align_up(M * c.d_model * 2);
         p.ssq1 = off; off += align_up(M * sizeof(float));
-        p.ssq2 = off; off += align_up(M * (size_t)(c.d_model / 128) * sizeof(float));
+        // partial sums of h^2: one per output column tile of the O projection
+        // (16 columns at the narrowest, token rows padded to 64 in decode)
+        p.ssq2 = off; off += align_up(std::max<size_t>(M, 64) * (size_t)(c.d_model / 16) * sizeof(float));
     }
     size_t scratch = 0;
     if (decode && c.wdtype == LLB_BF16) {
@@ -268,11 +271,40 @@ int tail_split(const llb_block* b, int cfg, const llb::GemmArgs& a) {
     return (int)(rounds * b->num_cus / pm) * bn;
 }
 
+// Most partial sums of squares the gate/up weight-streaming kernel gathers per
+// row (16 loads of 4 rows per thread).
+int max_ssq_parts(int M) { return M <= 32 ? 512 : 256; }
+
+// Decode (M <= 64) kernel of a projection C[M, N] = A W^T with epilogue epi:
+// the number of weight rows per workgroup of the narrow kernel, or 0 for the
+// 128-row split-K kernel.  Automatic choice (measured on MI355X, 8B and 70B
+// decode): the narrow kernel re-reads every token row per workgroup, so it
+// only pays where that operand is small, at most 32 token rows and K <= 4096
+// (the 8B QKV and O projections): 32 weight rows when that still occupies 3/4
+// of the CUs, else 16.  Everything else streams 128-row tiles with split-K.
+// An O projection (EPI_RESID_NORM) keeps its N / rows partial sums of squares
+// within what the gate/up kernel gathers.  `forced` >= 0 is the caller's
+// choice; -1 is returned when it does not fit.
+int decode_rows(const llb_block* b, int forced, int M, int N, int K, int epi) {
+    auto fits = [&](int rw) {
+        return llb::gemv_narrow_supports(M, N, K, epi, rw) &&
+               (epi != llb::EPI_RESID_NORM || N / rw <= max_ssq_parts(M));
+    };
+    if (forced == 0) return 0;
+    if (forced > 0) return fits(forced) ? forced : -1;
+    if (N / 128 >= 192 || M > 32 || K > 4096) return 0;
+    if (fits(32) && 4 * (N / 32) >= 3 * b->num_cus) return 32;
+    if (fits(16)) return 16;
+    return 0;
+}
+
 llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, float* scratch,
-                    int tile, bool auto_tile, hipStream_t s, const char* what) {
+                    int tile, bool auto_tile, hipStream_t s, const char* what, int rows = 0) {
     hipError_t e;
     if (b->cfg.wdtype == LLB_F32) {
         e = llb::gemm_f32_launch(a, s);
+    } else if (small_m && rows > 0) {
+        e = llb::gemv_narrow_launch(a, rows, b->num_cus, s);
     } else if (small_m) {
         const int sp = llb::gemv_bf16_splits(a.M, a.N, a.K);
         e = llb::gemv_bf16_launch(a, sp, scratch, s);
@@ -327,6 +359,13 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     const int tile_o = tile_for(b, b->tile_o, M, d, c.n_heads * hd, llb::EPI_RESID_NORM);
     const int tile_gu = tile_for(b, b->tile_gu, M, 2 * c.d_ff, d, llb::EPI_SWIGLU);
     const int tile_down = tile_for(b, b->tile_down, M, d, c.d_ff, llb::EPI_RESID);
+    const int hq = c.n_heads * hd;
+    const int rows_qkv = small_m ? decode_rows(b, b->dec_qkv, M, nqkv, d, llb::EPI_QKV) : 0;
+    const int rows_o = small_m ? decode_rows(b, b->dec_o, M, d, hq, llb::EPI_RESID_NORM) : 0;
+    const int rows_down = small_m ? decode_rows(b, b->dec_down, M, d, c.d_ff, llb::EPI_RESID) : 0;
+    if (bf16 && small_m && (rows_qkv < 0 || rows_o < 0 || rows_down < 0))
+        return fail(LLB_E_UNSUPPORTED, "decode kernel choice (%d, %d, %d) does not fit this block",
+                    b->dec_qkv, b->dec_o, b->dec_down);
     if (bf16 && !small_m) {
         // every projection's tile fits before anything is queued
         const struct { int cfg, N, K, epi; const char* what; } chk[] = {
@@ -368,7 +407,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = x; a.gain = b->g1; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_QKV; a.epi.q_out = q; a.epi.k_cache = kc; a.epi.v_cache = vc;
-    llb_status st = run_proj(b, a, small_m, scratch, tile_qkv, b->tile_qkv < 0, s, "qkv projection");
+    llb_status st = run_proj(b, a, small_m, scratch, tile_qkv, b->tile_qkv < 0, s, "qkv projection", rows_qkv);
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -397,12 +436,13 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
             llb::gemm_bf16_tile(tile_o, &bm, &bn, &nt);
             ssq2_count = d / bn;
         } else {
-            ssq2_count = llb::gemv_bf16_ssq_parts(d);  // one partial per 128-column tile
+            // one partial per column tile of the decode kernel
+            ssq2_count = rows_o > 0 ? d / rows_o : llb::gemv_bf16_ssq_parts(d);
         }
     } else {
         a.epi.kind = llb::EPI_RESID;
     }
-    st = run_proj(b, a, small_m, scratch, tile_o, b->tile_o < 0, s, "output projection");
+    st = run_proj(b, a, small_m, scratch, tile_o, b->tile_o < 0, s, "output projection", rows_o);
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -423,7 +463,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     a = llb::GemmArgs{};
     a.A = u; a.W = b->wdown; a.M = M; a.N = d; a.K = c.d_ff; a.eps = c.eps;
     a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = h; a.epi.out = y;
-    st = run_proj(b, a, small_m, scratch, tile_down, b->tile_down < 0, s, "down projection");
+    st = run_proj(b, a, small_m, scratch, tile_down, b->tile_down < 0, s, "down projection", rows_down);
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
     return LLB_OK;
@@ -474,6 +514,7 @@ llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* s
     b->cfg = c;
     b->es = c.wdtype == LLB_BF16 ? 2 : 4;
     b->tile_qkv = b->tile_o = b->tile_gu = b->tile_down = -1;
+    b->dec_qkv = b->dec_o = b->dec_down = -1;
     b->timing = 0;
     b->events_used = 0;
     hipError_t e = hipGetDevice(&b->device);
@@ -748,6 +789,17 @@ llb_status llb_block_set_tiles(llb_block* b, int32_t qkv, int32_t o, int32_t gat
     b->tile_o = o;
     b->tile_gu = gate_up;
     b->tile_down = down;
+    return LLB_OK;
+}
+
+llb_status llb_block_set_decode_rows(llb_block* b, int32_t qkv, int32_t o, int32_t down) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    for (int32_t v : {qkv, o, down})
+        if (v != -1 && v != 0 && v != 16 && v != 32)
+            return fail(LLB_E_INVALID, "decode kernel choice %d not in {-1, 0, 16, 32}", v);
+    b->dec_qkv = qkv;
+    b->dec_o = o;
+    b->dec_down = down;
     return LLB_OK;
 }
 

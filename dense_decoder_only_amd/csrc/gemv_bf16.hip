@@ -22,17 +22,77 @@ namespace {
 constexpr int GV_BN = 128;     // W rows per workgroup (4 waves x 32)
 constexpr int GV_BK = 64;      // k per pipeline stage (128-byte rows)
 constexpr int GV_NSTAGE = 6;
+constexpr int GV_MAXSPLIT = 8;  // most k-splits of one projection
 
 // 16-byte chunk c of a 128-byte LDS row r sits at c ^ ((r >> 1) & 7): the 16
 // lanes of a ds_read_b128 phase (16 consecutive rows, one chunk) hit distinct
 // banks.
 LLB_DEV int gv_swz(int r) { return (r >> 1) & 7; }
 
-LLB_DEV float row_scale(const GemmArgs& a, int m) {
+// Partial sums of squares of the decode projections are laid out [P][MT]:
+// partial p of token row m at ssq[p * MT + m], MT = 32 or 64 token rows held
+// by the kernels (an RMSNorm operand with one partial is the plain [M] row).
+
+// Serial inverse RMS of row m from P partials (the split-K reduction kernel).
+LLB_DEV float row_scale(const GemmArgs& a, int m, int MT) {
     float s = 0.f;
 #pragma unroll 8
-    for (int p = 0; p < a.ssq_count; ++p) s += a.ssq_in[(size_t)p * a.M + m];
+    for (int p = 0; p < a.ssq_count; ++p) s += a.ssq_in[(size_t)p * MT + m];
     return inv_rms(s, a.K, a.eps);
+}
+
+// The row scales of a normalised operand, gathered by the whole workgroup:
+// thread t loads partials p = g, g + G, ... (g = t / (MT/4), G = 1024 / MT)
+// of rows 4q..4q+3 (q = t % (MT/4)) with SL float4 loads, all issued at once
+// (partials past P re-read partial P-1 and are dropped), so that their latency
+// hides behind the weight copies.  finish() sums them in a fixed order into
+// out[m] = 1/rms of row m.  Needs P <= SL * G.
+template <int MT, int SL>
+struct RowScales {
+    static constexpr int Q = MT / 4, G = 256 / Q;
+    float4 v[SL];
+    LLB_DEV void issue(const GemmArgs& a) {
+        const int q = threadIdx.x % Q, g = threadIdx.x / Q;
+#pragma unroll
+        for (int i = 0; i < SL; ++i) {
+            const int p = min(g + i * G, a.ssq_count - 1);
+            v[i] = *(const float4*)(a.ssq_in + (size_t)p * MT + 4 * q);
+        }
+    }
+    // part: LDS scratch of 256 * 4 floats; out: LDS [MT].  Ends with a barrier.
+    LLB_DEV void finish(const GemmArgs& a, float* part, float* out) {
+        const int q = threadIdx.x % Q, g = threadIdx.x / Q;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < SL; ++i)
+            if (g + i * G < a.ssq_count) {
+                s.x += v[i].x; s.y += v[i].y; s.z += v[i].z; s.w += v[i].w;
+            }
+        *(float4*)(part + g * MT + 4 * q) = s;
+        __syncthreads();
+        if (threadIdx.x < MT) {
+            float t = 0.f;
+            for (int k = 0; k < G; ++k) t += part[k * MT + threadIdx.x];
+            out[threadIdx.x] = inv_rms(t, a.K, a.eps);
+        }
+        __syncthreads();
+    }
+};
+
+// s_waitcnt for a pipeline whose k-tiles are DPW copies each: `later` k-tiles
+// (0..MAXL) issued after the awaited one may stay in flight, plus EXTRA loads
+// issued after it.
+template <int DPW, int EXTRA, int MAXL>
+LLB_DEV void wait_later(int later) {
+    if constexpr (MAXL > 0) {
+        if (later >= MAXL) {
+            wait_vm_lgkm<MAXL * DPW + EXTRA>();
+            return;
+        }
+        wait_later<DPW, EXTRA, MAXL - 1>(later);
+    } else {
+        wait_vm_lgkm<EXTRA>();
+    }
 }
 
 template <int MS, int EPI>
@@ -84,21 +144,21 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
             dma16(src[i] + (size_t)j * (blk < W_BLK ? 8192 : GV_BK), st + (uint32_t)blk * 1024);
         }
     };
-    // wait until k-tile j has landed: min(GV_NSTAGE - 2, nk - 1 - j) later ones may stay in flight
+    // Row scales of the normalised-operand epilogues (one split only; with
+    // several the reduction kernel applies them): their loads go out right
+    // after the first copies, so the waits on those copies allow SL more.
+    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
+    constexpr int SL = EPI == EPI_SWIGLU ? 16 : 1;
+    static_assert((GV_NSTAGE - 2) * DPW + SL < 64, "vmcnt range");
+    const bool scaled = SCALED && splits == 1;
+    RowScales<MT, SL> rs;
+    // wait until k-tile j has landed: min(GV_NSTAGE - 2, nk - 1 - j) later ones
+    // may stay in flight, and the row-scale loads when j was issued before them
     auto wait_for = [&](int j) {
         const int later = min(GV_NSTAGE - 2, nk - 1 - j);
-        if (later >= 4) wait_vm_lgkm<4 * DPW>();
-        else if (later == 3) wait_vm_lgkm<3 * DPW>();
-        else if (later == 2) wait_vm_lgkm<2 * DPW>();
-        else if (later == 1) wait_vm_lgkm<DPW>();
-        else wait_vm_lgkm<0>();
+        if (scaled && j < GV_NSTAGE - 1) wait_later<DPW, SL, GV_NSTAGE - 2>(later);
+        else wait_later<DPW, 0, GV_NSTAGE - 2>(later);
     };
-
-    // row scale of the normalised-operand epilogues, loaded before the copies
-    // start (its loads are retired before the first wait on them)
-    constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
-    float my_scale = 1.0f;
-    if (SCALED && tid < M) my_scale = row_scale(args, tid);
 
     f32x16 acc[MS];
 #pragma unroll
@@ -112,6 +172,7 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
     typedef bf16x8 __attribute__((address_space(3))) * lds_frag_ptr;
 
     for (int j = 0; j < GV_NSTAGE - 1 && j < nk; ++j) issue(j);
+    if (scaled) rs.issue(args);
     for (int j = 0; j < nk; ++j) {
         wait_for(j);
         barrier();  // every wave is past k-tile j-1: its stage is free
@@ -148,9 +209,10 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
     // One split: the tile [M x 128] goes through LDS (fp32, reusing the stages)
     // to the epilogue.
     float* sred = (float*)smem;
-    static_assert(MT * GV_BN * 4 + MT * 4 <= GV_NSTAGE * STAGE, "tile fits in LDS");
+    static_assert(MT * GV_BN * 4 + MT * 4 + 1024 * 4 <= GV_NSTAGE * STAGE, "tile fits in LDS");
     float* sscale = sred + MT * GV_BN;
     __syncthreads();  // every wave is done with the stages
+    if (SCALED) rs.finish(args, sscale + MT, sscale);
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -158,7 +220,6 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
             const int tok = ms * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             sred[tok * GV_BN + wr] = acc[ms][r];
         }
-    if (SCALED && tid < M) sscale[tid] = my_scale;
     __syncthreads();
 
     const Epilogue& e = args.epi;
@@ -179,7 +240,7 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
             __syncthreads();
             if (tid == 0 || tid == 128) {
                 const int w0 = tid >> 6;
-                if (m < M) e.ssq_out[(size_t)tile * M + m] = s_ss[w0] + s_ss[w0 + 1];
+                if (m < M) e.ssq_out[(size_t)tile * MT + m] = s_ss[w0] + s_ss[w0 + 1];
             }
             __syncthreads();
         }
@@ -229,10 +290,17 @@ gemv_reduce_kernel(GemmArgs args, int splits, const float* __restrict__ part) {
     const int m = (blockIdx.x / tiles) * RPW + threadIdx.x / TPR;
     const int j = threadIdx.x % TPR;
     const int n0 = tile * GV_BN;
-    const float* tp = part + (size_t)tile * splits * MT * GV_BN + (size_t)m * GV_BN;
+    const float* tp = part + (size_t)tile * splits * MT * GV_BN + (size_t)min(m, M - 1) * GV_BN;
+    // the partials of up to GV_MAXSPLIT splits are loaded together (one memory
+    // round trip), then summed in split order
     auto col = [&](int c) {
-        float v = 0.f;
-        for (int sp = 0; sp < splits; ++sp) v += tp[(size_t)sp * MT * GV_BN + c];
+        float p[GV_MAXSPLIT];
+#pragma unroll
+        for (int sp = 0; sp < GV_MAXSPLIT; ++sp) p[sp] = tp[(size_t)min(sp, splits - 1) * MT * GV_BN + c];
+        float v = p[0];
+#pragma unroll
+        for (int sp = 1; sp < GV_MAXSPLIT; ++sp)
+            if (sp < splits) v += p[sp];
         return v;
     };
     const Epilogue& e = args.epi;
@@ -248,26 +316,233 @@ gemv_reduce_kernel(GemmArgs args, int splits, const float* __restrict__ part) {
         const int wave = threadIdx.x >> 6;
         if ((threadIdx.x & 63) == 0) s_ss[wave] = ss;
         __syncthreads();
-        if (j == 0 && m < M) e.ssq_out[(size_t)tile * M + m] = s_ss[2 * (wave >> 1)] + s_ss[2 * (wave >> 1) + 1];
+        if (j == 0 && m < M)
+            e.ssq_out[(size_t)tile * MT + m] = s_ss[2 * (wave >> 1)] + s_ss[2 * (wave >> 1) + 1];
     } else if constexpr (EPI == EPI_RESID) {
         if (m < M) epi_resid(e, m, n0 + j, N, col(j));
     } else if constexpr (EPI == EPI_LOGITS) {
-        if (m < M) e.out[(size_t)m * N + n0 + j] = col(j) * row_scale(args, m);
+        if (m < M) e.out[(size_t)m * N + n0 + j] = col(j) * row_scale(args, m, MT);
     } else if constexpr (EPI == EPI_SWIGLU) {
         if (m < M) {
             const int cg = (j >> 5) * 64 + (j & 31);
-            const float sc = row_scale(args, m);
+            const float sc = row_scale(args, m, MT);
             epi_swiglu<bf16_t>(e, m, n0 / 2 + j, N >> 1, col(cg) * sc, col(cg + 32) * sc);
         }
     } else {
         if (m < M) {
             const int c = 2 * j;
-            const float sc = row_scale(args, m);
+            const float sc = row_scale(args, m, MT);
             const float v0 = col(c) * sc, v1 = col(c + 1) * sc;
             epi_qkv<bf16_t>(e, m, n0 + c, v0, v1);
             epi_qkv<bf16_t>(e, m, n0 + c + 1, v1, v0);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Narrow weight streaming: one workgroup per RW (16 or 32) weight rows over the
+// whole of K, for projections whose N / 128 row tiles alone would not fill the
+// chip (a decode step's QKV, O and down projections).  Its four waves each
+// stream one quarter of K as independent pipelines: a wave copies its own
+// k-tiles (RW weight rows and the MT token rows, 64 columns each) global ->
+// LDS into a private ring of NS stages and multiplies them, with no workgroup
+// barrier in the main loop.  The four fp32 partial tiles are then summed
+// through LDS in wave order and the workgroup applies the epilogue itself, so
+// no partial ever leaves the CU.  RW = 16 uses 16x16x32 MFMAs, RW = 32 the
+// 32x32x16 ones.
+
+// Ring depth: as deep as LDS allows, for one workgroup per CU or (TWO) two.
+constexpr int narrow_ns(int rw, int ms, bool two) {
+    const int stage = (rw + 32 * ms) * GV_BK * 2;
+    const int ns = (two ? 75 * 1024 : 150 * 1024) / (4 * stage);
+    return ns > 6 ? 6 : ns < 2 ? 2 : ns;
+}
+
+template <int MS, int EPI, int RW, int NS>
+__global__ void __launch_bounds__(256)
+gemv_narrow_kernel(GemmArgs args) {
+    constexpr int MT = 32 * MS;
+    constexpr int W_BLK = RW / 8;       // 1 KB copy blocks per stage: 8 rows of 128 bytes
+    constexpr int A_BLK = MT / 8;
+    constexpr int DPW = W_BLK + A_BLK;  // a wave issues every copy of its stages
+    constexpr int STAGE = DPW * 1024;
+    constexpr bool SCALED = EPI == EPI_QKV;
+    constexpr int SL = 1;
+    static_assert(EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_RESID_NORM, "epilogue");
+    static_assert((NS - 2) * DPW + SL < 64, "vmcnt range");
+    static_assert(MT * RW * 4 <= NS * STAGE, "partial tile fits in a wave's ring");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * NS * STAGE];
+    __shared__ __attribute__((aligned(16))) float s_part[1024];
+    __shared__ float sscale[MT];
+
+    const int M = args.M, N = args.N, K = args.K;
+    const int n0 = blockIdx.x * RW;
+    const int nkt = K / GV_BK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kt0 = wave * nkt / 4;
+    const int nk = (wave + 1) * nkt / 4 - kt0;
+
+    const bf16_t* __restrict__ W = (const bf16_t*)args.W;
+    const bf16_t* __restrict__ A = (const bf16_t*)args.A;
+    // Copy block i of a stage: LDS rows 8i..8i+7 of [W rows; token rows], lane ->
+    // (row 8i + lane/8, LDS chunk lane%8) holding global chunk (lane%8) ^ swz(row).
+    // The RW rows of one k-tile are RW * 128 contiguous bytes of the 128 x 64
+    // tiled weight layout.
+    const bf16_t* src[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+        const int row = i * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ gv_swz(row);
+        if (i < W_BLK)
+            src[i] = W + ((size_t)(n0 >> 7) * nkt + kt0) * 8192 + ((n0 & 127) + row) * 64 + chunk * 8;
+        else
+            src[i] = A + (size_t)min(row - RW, M - 1) * K + (size_t)kt0 * GV_BK + chunk * 8;
+    }
+    const uint32_t ring = lds_offset(smem) + (uint32_t)wave * NS * STAGE;
+    auto issue = [&](int j) {  // k-tile kt0 + j into stage j % NS of this wave's ring
+        const uint32_t st = ring + (uint32_t)(j % NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+            dma16(src[i] + (size_t)j * (i < W_BLK ? 8192 : GV_BK), st + (uint32_t)i * 1024);
+    };
+
+    RowScales<MT, SL> rs;
+    for (int j = 0; j < NS - 1 && j < nk; ++j) issue(j);
+    if (SCALED) rs.issue(args);
+
+    constexpr int NACC = RW == 32 ? MS : 2 * MS;
+    f32x16 acc32[RW == 32 ? MS : 1];
+    f32x4 acc16[RW == 16 ? 2 * MS : 1];
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) {
+        if constexpr (RW == 32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc32[i][r] = 0.f;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc16[i][r] = 0.f;
+        }
+    }
+    typedef bf16x8 __attribute__((address_space(3))) * lds_frag_ptr;
+    auto frag = [&](uint32_t st, int row, int c) {
+        return *(lds_frag_ptr)(uintptr_t)(st + row * 128 + ((c ^ gv_swz(row)) << 4));
+    };
+
+    for (int j = 0; j < nk; ++j) {
+        // k-tile j has landed once at most min(NS - 2, nk - 1 - j) later k-tiles
+        // (and the row-scale loads, when j was issued before them) are in flight;
+        // the wait also retires this wave's LDS reads of the stage refilled next
+        const int later = min(NS - 2, nk - 1 - j);
+        if (SCALED && j < NS - 1) wait_later<DPW, SL, NS - 2>(later);
+        else wait_later<DPW, 0, NS - 2>(later);
+        if (j + NS - 1 < nk) issue(j + NS - 1);
+        const uint32_t st = ring + (uint32_t)(j % NS) * STAGE;
+        if constexpr (RW == 32) {
+            // lane: W row lane%32 / token row lane%32, chunk 2*kk + lane/32
+#pragma unroll
+            for (int kk = 0; kk < GV_BK / 16; ++kk) {
+                const int c = 2 * kk + (lane >> 5);
+                const bf16x8 wf = frag(st, lane & 31, c);
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+                    acc32[ms] = mfma32(frag(st, RW + ms * 32 + (lane & 31), c), wf, acc32[ms]);
+            }
+        } else {
+            // lane: W row lane%16 / token row lane%16, chunk 4*kk + lane/16
+#pragma unroll
+            for (int kk = 0; kk < GV_BK / 32; ++kk) {
+                const int c = 4 * kk + (lane >> 4);
+                const bf16x8 wf = frag(st, lane & 15, c);
+#pragma unroll
+                for (int tb = 0; tb < 2 * MS; ++tb)
+                    acc16[tb] = mfma16(frag(st, RW + tb * 16 + (lane & 15), c), wf, acc16[tb]);
+            }
+        }
+    }
+
+    // This wave's partial tile [MT][RW] (fp32) into its own ring: its copies
+    // have all landed and its reads have completed (the last wait was vmcnt(0)
+    // lgkmcnt(0)).  D layouts: 32x32 -> lane column lane%32, register r row
+    // 8*(r/4) + 4*(lane/32) + r%4; 16x16 -> lane column lane%16, register r row
+    // 4*(lane/16) + r.
+    float* part = (float*)(smem + wave * NS * STAGE);
+    if constexpr (RW == 32) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                part[(ms * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * RW + (lane & 31)] = acc32[ms][r];
+    } else {
+#pragma unroll
+        for (int tb = 0; tb < 2 * MS; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                part[(tb * 16 + 4 * (lane >> 4) + r) * RW + (lane & 15)] = acc16[tb][r];
+    }
+    __syncthreads();
+    if (SCALED) rs.finish(args, s_part, sscale);
+
+    // C[m, n0 + c] for 8 columns c0..c0+7, summed over the waves in order
+    const float* p0 = (const float*)smem;
+    auto cols8 = [&](int m, int c0, float* v) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = m * RW + c0 + k;
+            float s = p0[i];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) s += p0[w * (NS * STAGE / 4) + i];
+            v[k] = s;
+        }
+    };
+    const Epilogue& e = args.epi;
+    constexpr int TPR = RW / 8;  // threads per token row, 8 columns each
+    const int m = tid / TPR, c0 = (tid % TPR) * 8;
+    static_assert(256 / TPR >= 64, "one pass covers every token row");
+    float v[8];
+    if constexpr (EPI == EPI_QKV) {
+        if (m < M) {
+            cols8(m, c0, v);
+            const float sc = sscale[m];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] *= sc;
+            epi_qkv8(e, m, n0 + c0, v);
+        }
+    } else if constexpr (EPI == EPI_RESID) {
+        if (m < M) {
+            cols8(m, c0, v);
+            epi_resid8(e, m, n0 + c0, N, v);
+        }
+    } else {  // EPI_RESID_NORM: h, the next RMSNorm's operand, sum of h^2 over the RW columns
+        float ss = 0.f;
+        if (m < M) {
+            cols8(m, c0, v);
+            epi_resid8(e, m, n0 + c0, N, v);
+            ss = epi_norm_operand8(e, m, n0 + c0, N, v);
+        }
+#pragma unroll
+        for (int o = TPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if (m < M && c0 == 0) e.ssq_out[(size_t)blockIdx.x * MT + m] = ss;
+    }
+}
+
+template <int MS, int EPI, int RW, bool TWO>
+hipError_t launch_narrow(const GemmArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((gemv_narrow_kernel<MS, EPI, RW, narrow_ns(RW, MS, TWO)>), dim3(a.N / RW),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int MS, int EPI>
+hipError_t launch_narrow_rw(const GemmArgs& a, int rw, bool two, hipStream_t s) {
+    if (rw == 16) return two ? launch_narrow<MS, EPI, 16, true>(a, s) : launch_narrow<MS, EPI, 16, false>(a, s);
+    return two ? launch_narrow<MS, EPI, 32, true>(a, s) : launch_narrow<MS, EPI, 32, false>(a, s);
+}
+
+template <int EPI>
+hipError_t launch_narrow_epi(const GemmArgs& a, int rw, bool two, hipStream_t s) {
+    return a.M <= 32 ? launch_narrow_rw<1, EPI>(a, rw, two, s) : launch_narrow_rw<2, EPI>(a, rw, two, s);
 }
 
 template <int EPI>
@@ -300,7 +575,7 @@ int gemv_bf16_splits(int M, int N, int K) {
     const int nkt = K / GV_BK;
     const int target = 192;
     int s = (target + tiles - 1) / tiles;
-    s = std::max(1, std::min(s, nkt / 4));
+    s = std::max(1, std::min(std::min(s, nkt / 4), GV_MAXSPLIT));
     return s;
 }
 
@@ -310,7 +585,12 @@ size_t gemv_bf16_ws_bytes(int M, int N, int splits) {
 
 hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_t s) {
     if (a.M <= 0 || a.M > 64 || a.N % GV_BN != 0 || a.K % GV_BK != 0 || splits < 1 ||
-        splits > a.K / GV_BK)
+        splits > a.K / GV_BK || splits > GV_MAXSPLIT)
+        return hipErrorInvalidValue;
+    // one split gathers the row scales with RowScales: 16 (SwiGLU) or 1 loads per thread
+    const int groups = a.M <= 32 ? 32 : 16;
+    const bool scaled = a.epi.kind == EPI_QKV || a.epi.kind == EPI_SWIGLU || a.epi.kind == EPI_LOGITS;
+    if (scaled && splits == 1 && a.ssq_count > (a.epi.kind == EPI_SWIGLU ? 16 : 1) * groups)
         return hipErrorInvalidValue;
     switch (a.epi.kind) {
         case EPI_QKV: return launch_epi<EPI_QKV>(a, splits, ws, s);
@@ -323,6 +603,22 @@ hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_
 }
 
 int gemv_bf16_ssq_parts(int N) { return N / GV_BN; }
+
+bool gemv_narrow_supports(int M, int N, int K, int epi, int rw) {
+    return M >= 1 && M <= 64 && (rw == 16 || rw == 32) && N % GV_BN == 0 && K % GV_BK == 0 &&
+           K / GV_BK >= 4 && (epi == EPI_QKV || epi == EPI_RESID || epi == EPI_RESID_NORM);
+}
+
+hipError_t gemv_narrow_launch(const GemmArgs& a, int rw, int num_cus, hipStream_t s) {
+    if (!gemv_narrow_supports(a.M, a.N, a.K, a.epi.kind, rw)) return hipErrorInvalidValue;
+    if (a.epi.kind == EPI_QKV && a.ssq_count != 1) return hipErrorInvalidValue;
+    const bool two = a.N / rw > num_cus;  // more workgroups than CUs: two fit per CU
+    switch (a.epi.kind) {
+        case EPI_QKV: return launch_narrow_epi<EPI_QKV>(a, rw, two, s);
+        case EPI_RESID: return launch_narrow_epi<EPI_RESID>(a, rw, two, s);
+        default: return launch_narrow_epi<EPI_RESID_NORM>(a, rw, two, s);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // RMSNorm operand: one workgroup per row.  a[m, j] = bf16(x[m, j] * g[j]) (one

@@ -29,7 +29,8 @@ struct Epilogue {
     float* out;
     // EPI_RESID_NORM: as EPI_RESID, and also the next RMSNorm's operand
     // a_out[m, n] = bf16(out[m, n] * gain[n]) and the partial sum of out^2 over the
-    // tile's columns, ssq_out[tile_n * M + m] (one partial per column tile).
+    // tile's columns, one partial per column tile: ssq_out[tile_n * M + m] from
+    // the prefill GEMM, ssq_out[tile_n * MT + m] from the decode kernels.
     const float* gain;
     void* a_out;
     float* ssq_out;
@@ -43,8 +44,9 @@ struct Epilogue {
 // C = A . W^T.  W: [N, K], fp32 row-major or bf16 in the tiled layout below.
 // bf16 path: A is bf16 [M, K].  For EPI_QKV and EPI_SWIGLU, A holds v * g of an
 // RMSNorm (v the residual stream, g its gain) and the row's inverse RMS
-// 1/sqrt(sum/K + eps), sum = sum_p ssq_in[p*M + m] over ssq_count partials, scales
-// C before the epilogue.
+// 1/sqrt(sum/K + eps), sum over the ssq_count partials of ssq_in (laid out as
+// the producing kernel wrote them: [p][M] prefill, [p][MT] decode), scales C
+// before the epilogue.
 // fp32 path: A is fp32 [M, K]; when `norm`, the kernel forms the RMSNorm itself
 // (A * gain, row inverse RMS over K).
 struct GemmArgs {
@@ -81,11 +83,20 @@ hipError_t tile_weights_launch(const void* src, void* dst, int N, int K, hipStre
 // column tiles.  ws: gemv_bf16_ws_bytes(M, N, splits) bytes of fp32 partials.
 // With several splits a second kernel sums the partials in split order and
 // applies the epilogue.  EPI_RESID_NORM writes one partial sum of squares per
-// column tile, ssq_out[tile * M + m] (gemv_bf16_ssq_parts(N) of them).
+// column tile (gemv_bf16_ssq_parts(N) of them).  The decode kernels lay partial
+// sums of squares out as [P][MT], partial p of row m at ssq[p * MT + m] with
+// MT = 32 (M <= 32) or 64; a one-partial operand is the plain [M] row.
 size_t gemv_bf16_ws_bytes(int M, int N, int splits);
 int gemv_bf16_ssq_parts(int N);
 int gemv_bf16_splits(int M, int N, int K);
 hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_t s);
+// Narrow weight streaming (decode, M <= 64): one workgroup per rw (16 or 32) W
+// rows over all of K, its four waves splitting K and summing in LDS; epilogues
+// EPI_QKV, EPI_RESID, EPI_RESID_NORM in the same kernel (no partials in HBM).
+// EPI_RESID_NORM writes N / rw partial sums of squares.  Needs N % 128 == 0 (the
+// tiled weight layout) and K a multiple of 64 with K >= 256.
+bool gemv_narrow_supports(int M, int N, int K, int epi, int rw);
+hipError_t gemv_narrow_launch(const GemmArgs& a, int rw, int num_cus, hipStream_t s);
 
 // RMSNorm operand: a[m, :] = bf16(x[m, :] * g), ssq[m] = sum_j x[m, j]^2 (fp32).
 hipError_t norm_rows_launch(const float* x, const float* g, void* a, float* ssq, int M, int d,

@@ -245,6 +245,20 @@ int32_t llb_gemm_num_tiles(void);
 llb_status llb_gemm_tile_info(int32_t cfg, int32_t* bm, int32_t* bn);
 llb_status llb_block_set_tiles(llb_block* blk, int32_t qkv, int32_t o, int32_t gate_up, int32_t down);
 
+/* Tuning and test hook for the bf16 decode projections (llb_block_decode,
+ * llb_block_decode_ragged and the model's decode over at most 64 sequences).
+ * Each of the QKV, output and down projections streams its weights through one
+ * of two kernels: 0 = the split-K kernel (128 weight rows per workgroup, K
+ * split over workgroups, a second kernel summing the fp32 partials), 16 or 32
+ * = the narrow kernel with that many weight rows per workgroup over the whole
+ * of K (its four waves split K and sum in LDS, one kernel).  -1 restores the
+ * automatic choice.  The result is the same computation either way (parity
+ * with the oracle holds for every choice; bits may differ in the summation
+ * order).  Values outside {-1, 0, 16, 32} give LLB_E_INVALID and change
+ * nothing; a later decode call whose choice does not fit a projection's shape
+ * fails with LLB_E_UNSUPPORTED before any work is queued. */
+llb_status llb_block_set_decode_rows(llb_block* blk, int32_t qkv, int32_t o, int32_t down);
+
 /* Thread-local text describing the last non-OK status ("" if none). */
 const char* llb_last_error(void);
 

@@ -197,6 +197,52 @@ def test_bf16_decode_small(B, P, G):
     assert torch.all(kd[:, :, P + 1:].float() == SENTINEL)
 
 
+@pytest.mark.parametrize("B", [5, 40])
+@pytest.mark.parametrize("rows", [(0, 0, 0), (16, 16, 16), (32, 32, 32), (16, 32, 0)])
+@pytest.mark.parametrize("d,dff", [(512, 768), (1024, 2816)])
+def test_bf16_decode_kernel_choices(B, rows, d, dff):
+    """Every decode projection kernel against the oracle: the split-K kernel
+    (128 weight rows per workgroup, partials summed by a second kernel) and the
+    narrow kernel (16 or 32 weight rows per workgroup over all of K), for the
+    QKV (RoPE, cache write), O (residual, next RMSNorm's operand and partial
+    sums of squares, which the gate/up kernel gathers) and down projections;
+    B = 40 holds 64 token rows per tile."""
+    from dense_decoder_only_amd import llb
+    shp = shape(d_model=d, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=dff)
+    P = 150
+    cap = workloads.cache_capacity(P + 1)
+    w, x, kc, vc = gen_inputs(shp, 23 + B + d, B, 1, P, cap)
+    note(f"decode kernels {rows} B={B} d={d} d_ff={dff}")
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        llb.llb_block_set_decode_rows(gb.blk, *rows)
+        kd, vd = kc.cuda(), vc.cuda()
+        y = gb.decode(x.cuda(), kd, vd, P).cpu()
+        kd, vd = kd.cpu(), vd.cpu()
+    finally:
+        gb.close()
+    y_ref, k_ref, v_ref = oracle.block_forward(shp, w, x, kc, vc, P)
+    e_y = rel_err(y, y_ref)
+    e_k = bf16_err(kd[:, :, P:P + 1], k_ref)
+    e_v = bf16_err(vd[:, :, P:P + 1], v_ref)
+    note(f"  y {e_y:.2e} k {e_k:.3f} v {e_v:.3f}")
+    assert e_y <= 2e-2 and e_k <= 1.0 and e_v <= 1.0
+
+
+def test_decode_rows_rejects_bad_values():
+    from dense_decoder_only_amd import llb
+    shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+    w, _, _, _ = gen_inputs(shp, 3, 1, 1, 0, 64)
+    gb = GpuBlock(shp, w, max_positions=64)
+    try:
+        for bad in ((8, -1, -1), (-1, 64, -1), (-1, -1, -2)):
+            with pytest.raises(llb.LlbError):
+                llb.llb_block_set_decode_rows(gb.blk, *bad)
+        llb.llb_block_set_decode_rows(gb.blk)
+    finally:
+        gb.close()
+
+
 def _ragged_positions(B, P_max, seed):
     g = torch.Generator().manual_seed(seed)
     pos = torch.randint(0, P_max + 1, (B,), generator=g).tolist()
@@ -427,11 +473,12 @@ def test_bf16_prefill_is_deterministic():
         gb.close()
 
 
-def test_bf16_decode_split_k_with_dirty_workspace():
-    """The decode projections split K over workgroups and sum the partials in
-    split order through the workspace.  A workspace full of stale bytes, and
-    calls back to back on one workspace, give bit-identical results to a
-    zeroed one."""
+@pytest.mark.parametrize("rows", [-1, 0])
+def test_bf16_decode_split_k_with_dirty_workspace(rows):
+    """The decode projections sum split-K partials in a fixed order: in LDS
+    (narrow kernel, the automatic choice) or through the workspace (split-K
+    kernel).  A workspace full of stale bytes, and calls back to back on one
+    workspace, give bit-identical results to a zeroed one."""
     shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
     B, P = 7, 77
     cap = workloads.cache_capacity(P + 1)
@@ -440,6 +487,7 @@ def test_bf16_decode_split_k_with_dirty_workspace():
     gb = GpuBlock(shp, w, max_positions=cap)
     try:
         from dense_decoder_only_amd import llb
+        llb.llb_block_set_decode_rows(gb.blk, rows, rows, rows)
         ws = gb.workspace(B, 1)
         outs = []
         for fill in (0, 0xFF, 0x01, None, None):
