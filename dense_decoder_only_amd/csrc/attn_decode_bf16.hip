@@ -43,12 +43,13 @@ DecodePlan plan_decode(int B, int n_kv, int n_keys) {
     return p;
 }
 
-// One wave's share of a decode attention unit (sequence b, KV head g): keys
-// k_beg..k_end-1 for the G query heads of the group, in 16-key steps.  Leaves
-// the unnormalised partial state: m_run, l_run (every lane; base-2 units) and
-// o[h][0..7] = sum_n p_n v_n[8*pc .. 8*pc+8] in lanes pc = lane < HD/8.
+// One wave's share of a decode attention unit (sequence b, KV head g): the
+// 16-key steps starting at k_beg, k_beg + stride, ... below k_end, for the G
+// query heads of the group.  Leaves the unnormalised partial state: m_run,
+// l_run (every lane; base-2 units) and o[h][0..7] = sum_n p_n v_n[8*pc .. 8*pc+8]
+// in lanes pc = lane < HD/8.
 template <int HD, int G, int DEPTH>
-__device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, int k_beg, int k_end,
+__device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, int k_beg, int stride, int k_end,
                                              float (&sP)[16][16], float (&sAl)[16], float (&o)[G][8],
                                              float& m_run, float& l_run) {
     constexpr int KST = HD / 32;        // 16x16x32 MFMA steps over head_dim
@@ -170,7 +171,7 @@ __device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, in
     // exactly the DEPTH-1 younger steps.
     uint4 kf[DEPTH][KST], vf[DEPTH][KPL];
 #pragma unroll
-    for (int d = 0; d + 1 < DEPTH; ++d) load_step(k_beg + 16 * d, kf[d], vf[d]);
+    for (int d = 0; d + 1 < DEPTH; ++d) load_step(k_beg + stride * d, kf[d], vf[d]);
     // The query is consumed here, before the loop, so that no wait on it is
     // left inside the loop (heads past the group are zero columns).
 #pragma unroll
@@ -178,11 +179,11 @@ __device__ __forceinline__ void decode_chunk(const AttnArgs& a, int b, int g, in
         asm volatile("" ::"v"(qv[kk].x), "v"(qv[kk].y), "v"(qv[kk].z), "v"(qv[kk].w));
         qf[kk] = as_bf16x8(hq < G ? qv[kk] : make_uint4(0, 0, 0, 0));
     }
-    for (int kt = k_beg; kt < k_end; kt += 16 * DEPTH) {
+    for (int kt = k_beg; kt < k_end; kt += stride * DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-            const int kc = kt + 16 * d;
-            load_step(kc + 16 * (DEPTH - 1), kf[(d + DEPTH - 1) % DEPTH], vf[(d + DEPTH - 1) % DEPTH]);
+            const int kc = kt + stride * d;
+            load_step(kc + stride * (DEPTH - 1), kf[(d + DEPTH - 1) % DEPTH], vf[(d + DEPTH - 1) % DEPTH]);
             if (kc < k_end) step(kc, kf[d], vf[d]);
         }
     }
@@ -218,7 +219,7 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
     const int k_beg = ci * chunk;
     const int k_end = min(L, k_beg + chunk);
     float o[G][8], m_run, l_run;
-    decode_chunk<HD, G, 2>(a, b, g, k_beg, k_end, sP[wave], sAl[wave], o, m_run, l_run);
+    decode_chunk<HD, G, 2>(a, b, g, k_beg, 16, k_end, sP[wave], sAl[wave], o, m_run, l_run);
     const int pc = lane % NC;
     const size_t base = ((size_t)b * a.n_heads + (size_t)g * G) * n_chunks + ci;
     if (lane < NC) {
@@ -236,9 +237,11 @@ attn_decode_kernel(AttnArgs a, int n_chunks, int chunk, float* __restrict__ part
 }
 
 // One workgroup per unit (sequence b, KV head g) when there are enough units to
-// fill the GPU: AD_FW waves split the unit's keys into contiguous chunks and
-// their partial states are merged through LDS in wave order, so no partials
-// leave the workgroup and no second kernel is needed.
+// fill the GPU: AD_FW waves take the unit's 16-key steps in turn (wave w steps
+// w, w + AD_FW, ...: every wave streams from every part of the cache rows, so
+// the waves progress evenly, measured, where contiguous chunks finished up to
+// 1.7x apart) and their partial states are merged through LDS in wave order,
+// so no partials leave the workgroup and no second kernel is needed.
 constexpr int AD_FW = 8;
 
 template <int HD, int G>
@@ -254,11 +257,9 @@ attn_decode_fused_kernel(AttnArgs a) {
     const int g = blockIdx.x % a.n_kv;
     const int b = blockIdx.x / a.n_kv;
     const int L = (a.pos_b ? a.pos_b[b] : a.pos0) + 1;
-    const int chunk = ((L + AD_FW - 1) / AD_FW + 15) / 16 * 16;
-    const int k_beg = min(L, wave * chunk);
-    const int k_end = min(L, k_beg + chunk);
     float o[G][8], m_run, l_run;
-    decode_chunk<HD, G, (G <= 4 ? 3 : 2)>(a, b, g, k_beg, k_end, sP[wave], sAl[wave], o, m_run, l_run);
+    decode_chunk<HD, G, (G <= 4 ? 3 : 2)>(a, b, g, 16 * wave, 16 * AD_FW, L, sP[wave], sAl[wave], o, m_run,
+                                          l_run);
     if (lane < NC) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
