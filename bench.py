@@ -86,7 +86,7 @@ def stage_bytes(wl):
 
 
 # ------------------------------------------------------------- GPU timing
-def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None, decode_rows=None):
+def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None, decode_kernels=None):
     import torch
     import workloads
     from dense_decoder_only_amd import llb
@@ -103,8 +103,8 @@ def time_workload(name, steps, warmup, sets=1, warm_seconds=0.5, tiles=None, dec
         blocks.append(llb.llb_block_create(llb.make_config(shp, cap), w))
         if tiles is not None:
             llb.llb_block_set_tiles(blocks[-1], *tiles)
-        if decode_rows is not None:
-            llb.llb_block_set_decode_rows(blocks[-1], *decode_rows)
+        if decode_kernels is not None:
+            llb.llb_block_set_decode_kernels(blocks[-1], *decode_kernels)
         kc, vc = workloads.make_cache(shp, wl.B, workloads.max_start(wl), cap, gen, device=dev)
         caches.append((kc, vc))
     del w
@@ -302,9 +302,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--only", default=None, help="time only this workload (diagnostics)")
-    ap.add_argument("--decode-rows", default=None, metavar="Q,O,D",
-                    help="decode kernel of the QKV, O and down projections (-1 automatic, 0 split-K, "
-                         "16/32 narrow rows); with --only")
+    ap.add_argument("--decode-kernels", default=None, metavar="Q,O,GU,D",
+                    help="decode kernel of the QKV, O, gate/up and down projections (-1 automatic, "
+                         "0 split-K, 16/32 narrow rows); with --only")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the "
                          "HBM byte counters FETCH_SIZE / WRITE_SIZE against a known size)")
@@ -329,9 +329,9 @@ def main():
         return
 
     name = args.only or HEADLINE
-    drows = tuple(int(v) for v in args.decode_rows.split(",")) if args.decode_rows else None
+    drows = tuple(int(v) for v in args.decode_kernels.split(",")) if args.decode_kernels else None
     wl, ms, st = time_workload(name, args.steps, args.warmup, sets=2 if "decode" in name else 1,
-                               warm_seconds=args.warmup_seconds, decode_rows=drows)
+                               warm_seconds=args.warmup_seconds, decode_kernels=drows)
     head = summarize(wl, ms, st)
     log(f"{name}: {ms:.3f} ms/step, {head['tokens_per_s']:.0f} tok/s")
 

@@ -58,7 +58,7 @@ struct llb_block {
     float* g2;       // FFN RMSNorm gain, fp32 [d]
     float2* rope;    // [max_positions][hd/2] (cos, sin)
     int tile_qkv, tile_o, tile_gu, tile_down;  // bf16 prefill tile choice per projection (-1 = pick by M)
-    int dec_qkv, dec_o, dec_down;  // decode kernel per projection: -1 automatic, 0 split-K, 16/32 narrow rows
+    int dec_qkv, dec_o, dec_gu, dec_down;  // decode kernel per projection (llb_block_set_decode_kernels)
     int num_cus;                     // compute units of the device
     int timing;                      // record stage events on every call
     std::vector<hipEvent_t> events;  // 6 per recorded call
@@ -225,7 +225,9 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 //    projections (QKV, gate/up) the interleaved kernel on 16x16x32 MFMAs with
 //    the L2 prefetch, for the others the interleaved 32x32x16 kernel with the
 //    prefetch at long K and the 8-wave kernel otherwise;
-//  - 256x192 tiles when they fill whole rounds of the 256 compute units;
+//  - 256x192 tiles when they fill whole rounds of the 256 compute units (the
+//    QKV projection on the 16x16x32 prefetching kernel, others on the
+//    interleaved 32x32x16 kernel);
 //  - 256x256 tiles once they fill at least 160 compute units (gate/up on the
 //    16x16x32 prefetching kernel, the rest on the 8-wave kernel);
 //  - 256x128 tiles (interleaved, BK 64, 3 stages) from 192 tiles up when K is
@@ -235,7 +237,7 @@ int pick_tile(int M, int N, int K, int epi) {
     const bool scaled = epi == llb::EPI_QKV || epi == llb::EPI_SWIGLU;
     if (N % 256 == 0 && M >= 4096) return scaled ? 10 : (K >= 16384 || N >= 32768) ? 4 : 0;
     if (N % 128 != 0) return -1;
-    if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return 6;
+    if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 13 : 6;
     if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 10 : 0;
     const long t128 = (long)pm * (N / 128);
     if (t128 >= 192 && K % 64 == 0) return 7;
@@ -276,8 +278,8 @@ int tail_split(const llb_block* b, int cfg, const llb::GemmArgs& a) {
 int max_ssq_parts(int M) { return M <= 32 ? 512 : 256; }
 
 // Decode (M <= 64) kernel of a projection C[M, N] = A W^T with epilogue epi:
-// the number of weight rows per workgroup of the narrow kernel, or 0 for the
-// 128-row split-K kernel.  Automatic choice (measured on MI355X, 8B and 70B
+// the number of weight rows per workgroup of the narrow kernel (16 or 32), or
+// 0 for the 128-row split-K kernel.  Automatic choice (measured on MI355X, 8B and 70B
 // decode): the narrow kernel re-reads every token row per workgroup, so it
 // only pays where that operand is small, at most 32 token rows and K <= 4096
 // (the 8B QKV and O projections): 32 weight rows when that still occupies 3/4
@@ -363,9 +365,10 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     const int rows_qkv = small_m ? decode_rows(b, b->dec_qkv, M, nqkv, d, llb::EPI_QKV) : 0;
     const int rows_o = small_m ? decode_rows(b, b->dec_o, M, d, hq, llb::EPI_RESID_NORM) : 0;
     const int rows_down = small_m ? decode_rows(b, b->dec_down, M, d, c.d_ff, llb::EPI_RESID) : 0;
-    if (bf16 && small_m && (rows_qkv < 0 || rows_o < 0 || rows_down < 0))
-        return fail(LLB_E_UNSUPPORTED, "decode kernel choice (%d, %d, %d) does not fit this block",
-                    b->dec_qkv, b->dec_o, b->dec_down);
+    const int rows_gu = small_m ? decode_rows(b, b->dec_gu, M, 2 * c.d_ff, d, llb::EPI_SWIGLU) : 0;
+    if (bf16 && small_m && (rows_qkv < 0 || rows_o < 0 || rows_gu < 0 || rows_down < 0))
+        return fail(LLB_E_UNSUPPORTED, "decode kernel choice (%d, %d, %d, %d) does not fit this block",
+                    b->dec_qkv, b->dec_o, b->dec_gu, b->dec_down);
     if (bf16 && !small_m) {
         // every projection's tile fits before anything is queued
         const struct { int cfg, N, K, epi; const char* what; } chk[] = {
@@ -455,7 +458,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = h; a.gain = b->g2; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
-    st = run_proj(b, a, small_m, scratch, tile_gu, b->tile_gu < 0, s, "gate/up projection");
+    st = run_proj(b, a, small_m, scratch, tile_gu, b->tile_gu < 0, s, "gate/up projection", rows_gu);
     if (st != LLB_OK) return st;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -514,7 +517,7 @@ llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* s
     b->cfg = c;
     b->es = c.wdtype == LLB_BF16 ? 2 : 4;
     b->tile_qkv = b->tile_o = b->tile_gu = b->tile_down = -1;
-    b->dec_qkv = b->dec_o = b->dec_down = -1;
+    b->dec_qkv = b->dec_o = b->dec_gu = b->dec_down = -1;
     b->timing = 0;
     b->events_used = 0;
     hipError_t e = hipGetDevice(&b->device);
@@ -792,13 +795,17 @@ llb_status llb_block_set_tiles(llb_block* b, int32_t qkv, int32_t o, int32_t gat
     return LLB_OK;
 }
 
-llb_status llb_block_set_decode_rows(llb_block* b, int32_t qkv, int32_t o, int32_t down) {
+llb_status llb_block_set_decode_kernels(llb_block* b, int32_t qkv, int32_t o, int32_t gate_up,
+                                        int32_t down) {
     if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
     for (int32_t v : {qkv, o, down})
         if (v != -1 && v != 0 && v != 16 && v != 32)
             return fail(LLB_E_INVALID, "decode kernel choice %d not in {-1, 0, 16, 32}", v);
+    if (gate_up != -1 && gate_up != 0)
+        return fail(LLB_E_INVALID, "gate/up decode kernel choice %d not in {-1, 0}", gate_up);
     b->dec_qkv = qkv;
     b->dec_o = o;
+    b->dec_gu = gate_up;
     b->dec_down = down;
     return LLB_OK;
 }

@@ -95,6 +95,69 @@ LLB_DEV void wait_later(int later) {
     }
 }
 
+// The epilogue of one 128-column tile whose fp32 result sits in LDS: sred[tok *
+// 128 + c] for token rows tok < M, with the row scales in sscale[tok] (the
+// normalised-operand epilogues).  Called by all 256 threads of the workgroup.
+template <int MS, int EPI>
+LLB_DEV void gemv_tile_epilogue(const GemmArgs& args, const float* sred, const float* sscale, int tile) {
+    constexpr int MT = 32 * MS;
+    const int M = args.M, N = args.N;
+    const int n0 = tile * GV_BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const Epilogue& e = args.epi;
+    if constexpr (EPI == EPI_RESID_NORM) {
+        // two rows per pass, 128 threads (two waves) per row
+        __shared__ float s_ss[4];
+        for (int m0r = 0; m0r < M; m0r += 2) {
+            const int m = m0r + (tid >> 7);
+            const int c = tid & 127;
+            float ss = 0.f;
+            if (m < M) {
+                const float h = epi_resid(e, m, n0 + c, N, sred[m * GV_BN + c]);
+                epi_norm_operand(e, m, n0 + c, N, h);
+                ss = h * h;
+            }
+            ss = warp_sum(ss);
+            if (lane == 0) s_ss[wave] = ss;
+            __syncthreads();
+            if (tid == 0 || tid == 128) {
+                const int w0 = tid >> 6;
+                if (m < M) e.ssq_out[(size_t)tile * MT + m] = s_ss[w0] + s_ss[w0 + 1];
+            }
+            __syncthreads();
+        }
+    } else if constexpr (EPI == EPI_RESID) {
+        for (int idx = tid; idx < M * GV_BN; idx += 256) {
+            const int m = idx / GV_BN, c = idx % GV_BN;
+            epi_resid(e, m, n0 + c, N, sred[idx]);
+        }
+    } else if constexpr (EPI == EPI_LOGITS) {
+        for (int idx = tid; idx < M * GV_BN; idx += 256) {
+            const int m = idx / GV_BN, c = idx % GV_BN;
+            e.out[(size_t)m * N + n0 + c] = sred[idx] * sscale[m];
+        }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        // 128 columns = two groups [gate 32 | up 32]: 64 features per row
+        for (int idx = tid; idx < M * 64; idx += 256) {
+            const int m = idx / 64, j = idx % 64;
+            const int cg = (j >> 5) * 64 + (j & 31);
+            const float sc = sscale[m];
+            epi_swiglu<bf16_t>(e, m, n0 / 2 + j, N >> 1, sred[m * GV_BN + cg] * sc,
+                               sred[m * GV_BN + cg + 32] * sc);
+        }
+    } else {  // EPI_QKV: RoPE pairs
+        for (int idx = tid; idx < M * 64; idx += 256) {
+            const int m = idx / 64, c = 2 * (idx % 64);
+            const float sc = sscale[m];
+            const float v0 = sred[m * GV_BN + c] * sc, v1 = sred[m * GV_BN + c + 1] * sc;
+            epi_qkv<bf16_t>(e, m, n0 + c, v0, v1);
+            epi_qkv<bf16_t>(e, m, n0 + c + 1, v1, v0);
+        }
+    }
+}
+
 template <int MS, int EPI>
 __global__ void __launch_bounds__(256)
 gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
@@ -222,56 +285,7 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
         }
     __syncthreads();
 
-    const Epilogue& e = args.epi;
-    if constexpr (EPI == EPI_RESID_NORM) {
-        // two rows per pass, 128 threads (two waves) per row
-        __shared__ float s_ss[4];
-        for (int m0r = 0; m0r < M; m0r += 2) {
-            const int m = m0r + (tid >> 7);
-            const int c = tid & 127;
-            float ss = 0.f;
-            if (m < M) {
-                const float h = epi_resid(e, m, n0 + c, N, sred[m * GV_BN + c]);
-                epi_norm_operand(e, m, n0 + c, N, h);
-                ss = h * h;
-            }
-            ss = warp_sum(ss);
-            if (lane == 0) s_ss[wave] = ss;
-            __syncthreads();
-            if (tid == 0 || tid == 128) {
-                const int w0 = tid >> 6;
-                if (m < M) e.ssq_out[(size_t)tile * MT + m] = s_ss[w0] + s_ss[w0 + 1];
-            }
-            __syncthreads();
-        }
-    } else if constexpr (EPI == EPI_RESID) {
-        for (int idx = tid; idx < M * GV_BN; idx += 256) {
-            const int m = idx / GV_BN, c = idx % GV_BN;
-            epi_resid(e, m, n0 + c, N, sred[idx]);
-        }
-    } else if constexpr (EPI == EPI_LOGITS) {
-        for (int idx = tid; idx < M * GV_BN; idx += 256) {
-            const int m = idx / GV_BN, c = idx % GV_BN;
-            e.out[(size_t)m * N + n0 + c] = sred[idx] * sscale[m];
-        }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-        // 128 columns = two groups [gate 32 | up 32]: 64 features per row
-        for (int idx = tid; idx < M * 64; idx += 256) {
-            const int m = idx / 64, j = idx % 64;
-            const int cg = (j >> 5) * 64 + (j & 31);
-            const float sc = sscale[m];
-            epi_swiglu<bf16_t>(e, m, n0 / 2 + j, N >> 1, sred[m * GV_BN + cg] * sc,
-                               sred[m * GV_BN + cg + 32] * sc);
-        }
-    } else {  // EPI_QKV: RoPE pairs
-        for (int idx = tid; idx < M * 64; idx += 256) {
-            const int m = idx / 64, c = 2 * (idx % 64);
-            const float sc = sscale[m];
-            const float v0 = sred[m * GV_BN + c] * sc, v1 = sred[m * GV_BN + c + 1] * sc;
-            epi_qkv<bf16_t>(e, m, n0 + c, v0, v1);
-            epi_qkv<bf16_t>(e, m, n0 + c + 1, v1, v0);
-        }
-    }
+    gemv_tile_epilogue<MS, EPI>(args, sred, sscale, tile);
 }
 
 // Sums the split partials of one column tile in split order and applies the

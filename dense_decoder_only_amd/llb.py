@@ -32,7 +32,7 @@ STATUS_NAMES = {0: "LLB_OK", -1: "LLB_E_INVALID", -2: "LLB_E_UNSUPPORTED", -3: "
 EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes",
             "llb_block_prefill", "llb_block_prefill_at", "llb_block_decode", "llb_block_decode_ragged", "llb_kv_append", "llb_attention_prefill",
             "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
-            "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles", "llb_block_set_decode_rows",
+            "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles", "llb_block_set_decode_kernels",
             "llb_model_create", "llb_model_destroy", "llb_model_workspace_bytes", "llb_model_forward",
             "llb_last_error")
 
@@ -107,8 +107,8 @@ def load_library(path: str = LIB_PATH):
     lib.llb_gemm_tile_info.restype = ctypes.c_int
     lib.llb_block_set_tiles.argtypes = [vp, i32, i32, i32, i32]
     lib.llb_block_set_tiles.restype = ctypes.c_int
-    lib.llb_block_set_decode_rows.argtypes = [vp, i32, i32, i32]
-    lib.llb_block_set_decode_rows.restype = ctypes.c_int
+    lib.llb_block_set_decode_kernels.argtypes = [vp, i32, i32, i32, i32]
+    lib.llb_block_set_decode_kernels.restype = ctypes.c_int
     lib.llb_model_create.argtypes = [ctypes.POINTER(llb_config), i32, i32, vp, ctypes.POINTER(llb_weights), vp, vp,
                                      vp, ctypes.POINTER(vp)]
     lib.llb_model_create.restype = ctypes.c_int
@@ -322,8 +322,9 @@ def llb_block_set_tiles(blk: Block, qkv: int = -1, o: int = -1, gate_up: int = -
     _check(load_library().llb_block_set_tiles(blk.handle, qkv, o, gate_up, down), "llb_block_set_tiles")
 
 
-def llb_block_set_decode_rows(blk: Block, qkv: int = -1, o: int = -1, down: int = -1) -> None:
-    _check(load_library().llb_block_set_decode_rows(blk.handle, qkv, o, down), "llb_block_set_decode_rows")
+def llb_block_set_decode_kernels(blk: Block, qkv: int = -1, o: int = -1, gate_up: int = -1, down: int = -1) -> None:
+    _check(load_library().llb_block_set_decode_kernels(blk.handle, qkv, o, gate_up, down),
+           "llb_block_set_decode_kernels")
 
 
 def llb_block_set_stage_timing(blk: Block, enable: bool) -> None:

@@ -247,17 +247,20 @@ llb_status llb_block_set_tiles(llb_block* blk, int32_t qkv, int32_t o, int32_t g
 
 /* Tuning and test hook for the bf16 decode projections (llb_block_decode,
  * llb_block_decode_ragged and the model's decode over at most 64 sequences).
- * Each of the QKV, output and down projections streams its weights through one
- * of two kernels: 0 = the split-K kernel (128 weight rows per workgroup, K
- * split over workgroups, a second kernel summing the fp32 partials), 16 or 32
- * = the narrow kernel with that many weight rows per workgroup over the whole
- * of K (its four waves split K and sum in LDS, one kernel).  -1 restores the
- * automatic choice.  The result is the same computation either way (parity
- * with the oracle holds for every choice; bits may differ in the summation
- * order).  Values outside {-1, 0, 16, 32} give LLB_E_INVALID and change
- * nothing; a later decode call whose choice does not fit a projection's shape
- * fails with LLB_E_UNSUPPORTED before any work is queued. */
-llb_status llb_block_set_decode_rows(llb_block* blk, int32_t qkv, int32_t o, int32_t down);
+ * Each projection streams its weights through one of two kernels:
+ *   0  = split-K, 128 weight rows per workgroup, weights and token rows staged
+ *        through LDS by DMA; with K split over workgroups a second kernel sums
+ *        the fp32 partials in split order;
+ *   16, 32 = narrow: that many weight rows per workgroup over the whole of K
+ *        (its four waves split K and sum in LDS; one kernel); QKV, O and down
+ *        only (the gate/up pairs need 64-row groups).
+ * -1 restores the automatic choice.  Every choice computes the same products;
+ * results differ only in summation order (parity with the oracle holds for
+ * each).  Values outside those sets give LLB_E_INVALID and change nothing; a
+ * later decode call whose choice does not fit a projection's shape fails with
+ * LLB_E_UNSUPPORTED before any work is queued. */
+llb_status llb_block_set_decode_kernels(llb_block* blk, int32_t qkv, int32_t o, int32_t gate_up,
+                                        int32_t down);
 
 /* Thread-local text describing the last non-OK status ("" if none). */
 const char* llb_last_error(void);

@@ -198,9 +198,9 @@ def test_bf16_decode_small(B, P, G):
 
 
 @pytest.mark.parametrize("B", [5, 40])
-@pytest.mark.parametrize("rows", [(0, 0, 0), (16, 16, 16), (32, 32, 32), (16, 32, 0)])
+@pytest.mark.parametrize("kernels", [(0, 0, 0, 0), (16, 16, 0, 16), (32, 32, -1, 32), (16, 32, 0, 0)])
 @pytest.mark.parametrize("d,dff", [(512, 768), (1024, 2816)])
-def test_bf16_decode_kernel_choices(B, rows, d, dff):
+def test_bf16_decode_kernel_choices(B, kernels, d, dff):
     """Every decode projection kernel against the oracle: the split-K kernel
     (128 weight rows per workgroup, partials summed by a second kernel) and the
     narrow kernel (16 or 32 weight rows per workgroup over all of K), for the
@@ -212,10 +212,10 @@ def test_bf16_decode_kernel_choices(B, rows, d, dff):
     P = 150
     cap = workloads.cache_capacity(P + 1)
     w, x, kc, vc = gen_inputs(shp, 23 + B + d, B, 1, P, cap)
-    note(f"decode kernels {rows} B={B} d={d} d_ff={dff}")
+    note(f"decode kernels {kernels} B={B} d={d} d_ff={dff}")
     gb = GpuBlock(shp, w, max_positions=cap)
     try:
-        llb.llb_block_set_decode_rows(gb.blk, *rows)
+        llb.llb_block_set_decode_kernels(gb.blk, *kernels)
         kd, vd = kc.cuda(), vc.cuda()
         y = gb.decode(x.cuda(), kd, vd, P).cpu()
         kd, vd = kd.cpu(), vd.cpu()
@@ -229,16 +229,16 @@ def test_bf16_decode_kernel_choices(B, rows, d, dff):
     assert e_y <= 2e-2 and e_k <= 1.0 and e_v <= 1.0
 
 
-def test_decode_rows_rejects_bad_values():
+def test_decode_kernels_rejects_bad_values():
     from dense_decoder_only_amd import llb
     shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
     w, _, _, _ = gen_inputs(shp, 3, 1, 1, 0, 64)
     gb = GpuBlock(shp, w, max_positions=64)
     try:
-        for bad in ((8, -1, -1), (-1, 64, -1), (-1, -1, -2)):
+        for bad in ((8, -1, -1, -1), (-1, 64, -1, -1), (-1, -1, -1, -2), (-1, -1, 16, -1), (1, -1, -1, -1)):
             with pytest.raises(llb.LlbError):
-                llb.llb_block_set_decode_rows(gb.blk, *bad)
-        llb.llb_block_set_decode_rows(gb.blk)
+                llb.llb_block_set_decode_kernels(gb.blk, *bad)
+        llb.llb_block_set_decode_kernels(gb.blk)
     finally:
         gb.close()
 
@@ -473,11 +473,10 @@ def test_bf16_prefill_is_deterministic():
         gb.close()
 
 
-@pytest.mark.parametrize("rows", [-1, 0])
-def test_bf16_decode_split_k_with_dirty_workspace(rows):
+@pytest.mark.parametrize("kern", [-1, 0])
+def test_bf16_decode_split_k_with_dirty_workspace(kern):
     """The decode projections sum split-K partials in a fixed order: in LDS
-    (narrow kernel, the automatic choice) or through the workspace (split-K
-    kernel).  A workspace full of stale bytes, and calls back to back on one
+    (narrow kernel) or through the workspace (split-K kernels).  A workspace full of stale bytes, and calls back to back on one
     workspace, give bit-identical results to a zeroed one."""
     shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
     B, P = 7, 77
@@ -487,7 +486,7 @@ def test_bf16_decode_split_k_with_dirty_workspace(rows):
     gb = GpuBlock(shp, w, max_positions=cap)
     try:
         from dense_decoder_only_amd import llb
-        llb.llb_block_set_decode_rows(gb.blk, rows, rows, rows)
+        llb.llb_block_set_decode_kernels(gb.blk, kern, kern, kern, kern)
         ws = gb.workspace(B, 1)
         outs = []
         for fill in (0, 0xFF, 0x01, None, None):
