@@ -530,9 +530,6 @@ constexpr TileCfg kTiles[] = {
     {256, 128, 2, 2, 64, 3, 1, 3},  // 7 on 16x16x32 MFMAs
     {256, 192, 2, 2, 64, 2, 1, 3},  // 6 on 16x16x32 MFMAs
     {256, 192, 2, 2, 64, 2, 1, 4},  // 12 with the L2 prefetch
-    {256, 128, 2, 2, 64, 3, 1, 4},  // 11 with the L2 prefetch
-    {256, 192, 2, 2, 64, 2, 1, 2},  // 6 with the L2 prefetch
-    {256, 128, 2, 2, 64, 3, 1, 2},  // 7 with the L2 prefetch
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -614,10 +611,7 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
         case 10: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
         case 11: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_I16>(a, s);
         case 12: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16>(a, s);
-        case 13: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
-        case 14: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_I16_PF>(a, s);
-        case 15: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_INTERLEAVE_PF>(a, s);
-        default: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_INTERLEAVE_PF>(a, s);
+        default: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
     }
 }
 
