@@ -187,7 +187,9 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
     if (c.wdtype == LLB_BF16) {
         p.a1 = off; off += align_up(M * c.d_model * 2);
         p.a2 = off; off += align_up(M * c.d_model * 2);
-        p.ssq1 = off; off += align_up(M * sizeof(float));
+        // row sums of squares of x: one, or the partials a previous block's down
+        // projection wrote (one per output column tile, token rows padded to 64)
+        p.ssq1 = off; off += align_up(std::max<size_t>(M, 64) * (size_t)(c.d_model / 16) * sizeof(float));
         // partial sums of h^2: one per output column tile of the O projection
         // (16 columns at the narrowest, token rows padded to 64 in decode)
         p.ssq2 = off; off += align_up(std::max<size_t>(M, 64) * (size_t)(c.d_model / 16) * sizeof(float));
@@ -329,6 +331,20 @@ llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, fl
     return LLB_OK;
 }
 
+// Blocks run back to back (a model) hand the attention RMSNorm of the next
+// block to the down projection of this one: its epilogue writes, besides
+// y = h + down, the next block's operand bf16(y * g1') and partial sums of y^2
+// into the workspace's a1 / ssq1, which the next call (same workspace) uses
+// instead of running the norm kernel.
+struct NormChain {
+    int in_parts;          // > 0: a1 / ssq1 already hold this block's operand and that many partials
+    const float* out_gain; // non-null: also write the next block's operand with this gain
+    int out_parts;         // set by run_block: partials written (0: the next block normalises itself)
+};
+
+// Most row-sum partials the decode QKV kernels gather (4 float4 loads per thread).
+int qkv_max_parts(int M) { return 4 * (M <= 32 ? 32 : 16); }
+
 // The kernel sequence of one block call over M = B*T tokens at positions
 // pos0..pos0+T-1 ("Llama 3.1 70B", section "Transformer layer"):
 //   h = x + Wo . Attn(RMSNorm(x)),  y = h + Wdown . SwiGLU(RMSNorm(h)).
@@ -336,7 +352,7 @@ llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, fl
 // every sequence starts at pos0.  With them, pos0 is their maximum.
 llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int pos0, void* kc,
                      void* vc, int cap, void* ws, size_t ws_bytes, hipStream_t s, bool decode,
-                     const int32_t* pos_host = nullptr) {
+                     const int32_t* pos_host = nullptr, NormChain* chain = nullptr) {
     const llb_config& c = b->cfg;
     const int L = pos0 + T;
     const WsPlan p = plan_ws(b, B, T, decode, L);
@@ -402,7 +418,10 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     // 1. RMSNorm(x) . Wqkv^T, RoPE, Q -> workspace, K/V -> cache rows pos0..pos0+T-1
     llb::GemmArgs a{};
     a.W = b->wqkv; a.M = M; a.N = nqkv; a.K = d; a.eps = c.eps;
-    if (bf16) {
+    if (bf16 && chain && chain->in_parts > 0) {
+        // the previous block's down projection wrote the operand and the partials
+        a.A = a1; a.ssq_in = ssq1; a.ssq_count = chain->in_parts;
+    } else if (bf16) {
         hipError_t ne = llb::norm_rows_launch(x, b->g1, a1, ssq1, M, d, s);
         if (ne != hipSuccess) return hip_fail(ne, "attention RMSNorm");
         a.A = a1; a.ssq_in = ssq1; a.ssq_count = 1;
@@ -466,8 +485,26 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     a = llb::GemmArgs{};
     a.A = u; a.W = b->wdown; a.M = M; a.N = d; a.K = c.d_ff; a.eps = c.eps;
     a.epi = e; a.epi.kind = llb::EPI_RESID; a.epi.resid = h; a.epi.out = y;
+    int out_parts = 0;
+    if (bf16 && chain && chain->out_gain) {
+        // the next block's RMSNorm operand too, when the down projection's
+        // kernel has that epilogue and the next QKV kernel can gather the partials
+        if (small_m) {
+            const int parts = rows_down > 0 ? d / rows_down : llb::gemv_bf16_ssq_parts(d);
+            if (parts <= qkv_max_parts(M)) out_parts = parts;
+        } else if (llb::gemm_bf16_supports(tile_down, d, c.d_ff, llb::EPI_RESID_NORM)) {
+            int bm, bn, nt;
+            llb::gemm_bf16_tile(tile_down, &bm, &bn, &nt);
+            out_parts = d / bn;
+        }
+        if (out_parts > 0) {
+            a.epi.kind = llb::EPI_RESID_NORM;
+            a.epi.gain = chain->out_gain; a.epi.a_out = a1; a.epi.ssq_out = ssq1;
+        }
+    }
     st = run_proj(b, a, small_m, scratch, tile_down, b->tile_down < 0, s, "down projection", rows_down);
     if (st != LLB_OK) return st;
+    if (chain) chain->out_parts = out_parts;
     if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
     return LLB_OK;
 }
@@ -981,13 +1018,15 @@ llb_status llb_model_forward(llb_model* m, const int32_t* tokens, int32_t B, int
     const int d = m->cfg.d_model, M = B * T;
     hipError_t e = llb::embed_launch(tokens, m->embed, x, M, d, m->vocab, s);
     if (e != hipSuccess) return hip_fail(e, "embedding");
+    // the blocks, in place on x, each handing the next one its attention RMSNorm
+    // (positions and buffers were checked above)
+    int parts = 0;
     for (int l = 0; l < m->n_layers; ++l) {
-        const llb_status st =
-            T == 1 ? llb_block_decode(m->layers[l], x, x, B, start_pos, k_caches[l], v_caches[l], cache_cap,
-                                      w + p.blk, p.blk_bytes, stream)
-                   : llb_block_prefill_at(m->layers[l], x, x, B, T, start_pos, k_caches[l], v_caches[l],
-                                          cache_cap, w + p.blk, p.blk_bytes, stream);
+        NormChain ch{parts, l + 1 < m->n_layers ? m->layers[l + 1]->g1 : nullptr, 0};
+        const llb_status st = run_block(m->layers[l], x, x, B, T, start_pos, k_caches[l], v_caches[l],
+                                        cache_cap, w + p.blk, p.blk_bytes, s, T == 1, nullptr, &ch);
         if (st != LLB_OK) return st;
+        parts = ch.out_parts;
     }
     const float* src = x;
     int R = M;

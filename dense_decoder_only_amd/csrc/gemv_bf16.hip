@@ -211,7 +211,7 @@ gemv_bf16_kernel(GemmArgs args, int splits, float* __restrict__ part) {
     // several the reduction kernel applies them): their loads go out right
     // after the first copies, so the waits on those copies allow SL more.
     constexpr bool SCALED = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
-    constexpr int SL = EPI == EPI_SWIGLU ? 16 : 1;
+    constexpr int SL = EPI == EPI_SWIGLU ? 16 : 4;
     static_assert((GV_NSTAGE - 2) * DPW + SL < 64, "vmcnt range");
     const bool scaled = SCALED && splits == 1;
     RowScales<MT, SL> rs;
@@ -381,7 +381,7 @@ gemv_narrow_kernel(GemmArgs args) {
     constexpr int DPW = W_BLK + A_BLK;  // a wave issues every copy of its stages
     constexpr int STAGE = DPW * 1024;
     constexpr bool SCALED = EPI == EPI_QKV;
-    constexpr int SL = 1;
+    constexpr int SL = 4;
     static_assert(EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_RESID_NORM, "epilogue");
     static_assert((NS - 2) * DPW + SL < 64, "vmcnt range");
     static_assert(MT * RW * 4 <= NS * STAGE, "partial tile fits in a wave's ring");
@@ -601,10 +601,10 @@ hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_
     if (a.M <= 0 || a.M > 64 || a.N % GV_BN != 0 || a.K % GV_BK != 0 || splits < 1 ||
         splits > a.K / GV_BK || splits > GV_MAXSPLIT)
         return hipErrorInvalidValue;
-    // one split gathers the row scales with RowScales: 16 (SwiGLU) or 1 loads per thread
+    // one split gathers the row scales with RowScales: 16 (SwiGLU) or 4 loads per thread
     const int groups = a.M <= 32 ? 32 : 16;
     const bool scaled = a.epi.kind == EPI_QKV || a.epi.kind == EPI_SWIGLU || a.epi.kind == EPI_LOGITS;
-    if (scaled && splits == 1 && a.ssq_count > (a.epi.kind == EPI_SWIGLU ? 16 : 1) * groups)
+    if (scaled && splits == 1 && a.ssq_count > (a.epi.kind == EPI_SWIGLU ? 16 : 4) * groups)
         return hipErrorInvalidValue;
     switch (a.epi.kind) {
         case EPI_QKV: return launch_epi<EPI_QKV>(a, splits, ws, s);
@@ -625,7 +625,7 @@ bool gemv_narrow_supports(int M, int N, int K, int epi, int rw) {
 
 hipError_t gemv_narrow_launch(const GemmArgs& a, int rw, int num_cus, hipStream_t s) {
     if (!gemv_narrow_supports(a.M, a.N, a.K, a.epi.kind, rw)) return hipErrorInvalidValue;
-    if (a.epi.kind == EPI_QKV && a.ssq_count != 1) return hipErrorInvalidValue;
+    if (a.epi.kind == EPI_QKV && a.ssq_count > 4 * (a.M <= 32 ? 32 : 16)) return hipErrorInvalidValue;
     const bool two = a.N / rw > num_cus;  // more workgroups than CUs: two fit per CU
     switch (a.epi.kind) {
         case EPI_QKV: return launch_narrow_epi<EPI_QKV>(a, rw, two, s);

@@ -449,6 +449,38 @@ def test_chunked_prefill_rejects_bad_positions():
         gb.close()
 
 
+def test_empty_inputs_are_rejected_before_any_launch():
+    """B = 0 or T = 0 (an empty batch) is an argument error on every entry point,
+    reported before anything is queued: the cache is untouched and the
+    workspace size query answers 0."""
+    from dense_decoder_only_amd import llb
+    shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+    cap = 64
+    w, x, kc, vc = gen_inputs(shp, 4, 2, 8, 8, cap)
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        kd, vd, xd = kc.cuda(), vc.cuda(), x.cuda()
+        y = torch.empty_like(xd)
+        ws = gb.workspace(2, 8)
+        assert llb.llb_block_workspace_bytes(gb.blk, 0, 8) == 0
+        assert llb.llb_block_workspace_bytes(gb.blk, 2, 0) == 0
+        calls = [
+            lambda: llb.llb_block_prefill(gb.blk, xd, y, 0, 8, kd, vd, cap, ws),
+            lambda: llb.llb_block_prefill(gb.blk, xd, y, 2, 0, kd, vd, cap, ws),
+            lambda: llb.llb_block_prefill_at(gb.blk, xd, y, 2, 0, 8, kd, vd, cap, ws),
+            lambda: llb.llb_block_decode(gb.blk, xd, y, 0, 8, kd, vd, cap, ws),
+            lambda: llb.llb_block_decode_ragged(gb.blk, xd, y, 0, [], kd, vd, cap, ws),
+        ]
+        for call in calls:
+            with pytest.raises(llb.LlbError) as ei:
+                call()
+            assert ei.value.status == llb.LLB_E_INVALID
+        torch.cuda.synchronize()
+        assert torch.equal(kd.cpu(), kc) and torch.equal(vd.cpu(), vc)
+    finally:
+        gb.close()
+
+
 def test_bf16_prefill_is_deterministic():
     shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
     B, T = 2, 130
