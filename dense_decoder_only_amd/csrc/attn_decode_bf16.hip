@@ -14,6 +14,8 @@
 // each lane owning 8 output dims of one key slot.  Each chunk leaves an
 // unnormalised (m, l, o) partial; a second kernel merges the chunks of a head in
 // chunk order (log-sum-exp rescaling), so results do not depend on timing.
+#include <algorithm>
+
 #include "common.cuh"
 #include "kernels.h"
 
@@ -319,9 +321,15 @@ hipError_t launch_g(const AttnArgs& a, const DecodePlan& p, float* part_o, float
 
 }  // namespace
 
+// Partials of the split form for any call reading at most n_keys keys: the
+// chunk count of plan_decode is at most min(target chunks per unit, n_keys/16
+// rounded up), a bound that grows with n_keys (the chunk count itself does not:
+// 1001 keys over 256 units take 16 chunks, 1088 keys 14).
 size_t attn_decode_ws_bytes(int B, int n_heads, int n_kv, int hd, int n_keys) {
-    const DecodePlan p = plan_decode(B, n_kv, n_keys);
-    return (size_t)B * n_heads * p.n_chunks * (hd + 2) * sizeof(float);
+    const int units = B * n_kv;
+    const int n_target = (AD_TARGET_WAVES + units - 1) / units;
+    const int chunks = std::max(1, std::min(n_target, (n_keys + 15) / 16));
+    return (size_t)B * n_heads * chunks * (hd + 2) * sizeof(float);
 }
 
 template <int G>

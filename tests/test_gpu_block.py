@@ -449,6 +449,34 @@ def test_chunked_prefill_rejects_bad_positions():
         gb.close()
 
 
+def test_decode_workspace_query_covers_every_position():
+    """llb_block_workspace_bytes(B, 1) covers a decode at any start position
+    below max_positions: the split attention's chunk count is not monotone in
+    the key count (here 1001 keys need more chunks than 1088), so the query
+    must return a bound, not the size at max_positions.  A workspace of exactly
+    the advertised size decodes at P = 1000, 1087 and 0."""
+    from dense_decoder_only_amd import llb
+    shp = shape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
+    B, cap = 64, 1088
+    w, x, kc, vc = gen_inputs(shp, 31, B, 1, cap - 1, cap)
+    note("decode workspace bound")
+    gb = GpuBlock(shp, w, max_positions=cap)
+    try:
+        n = llb.llb_block_workspace_bytes(gb.blk, B, 1)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        xd = x.cuda()
+        for P in (1000, cap - 1, 0):
+            kd, vd = kc.cuda(), vc.cuda()
+            y = torch.empty_like(xd)
+            llb.llb_block_decode(gb.blk, xd, y, B, P, kd, vd, cap, ws)
+            if P == 1000:
+                y_ref, _, _ = oracle.block_forward(shp, w, x, kc, vc, P)
+                assert rel_err(y.cpu(), y_ref) <= 2e-2
+        torch.cuda.synchronize()
+    finally:
+        gb.close()
+
+
 def test_empty_inputs_are_rejected_before_any_launch():
     """B = 0 or T = 0 (an empty batch) is an argument error on every entry point,
     reported before anything is queued: the cache is untouched and the
