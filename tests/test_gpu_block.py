@@ -173,7 +173,7 @@ def test_tile_override_rejects_bad_values():
         gb.close()
 
 
-@pytest.mark.parametrize("B,P,G", [(5, 300, 4), (40, 64, 4), (70, 20, 4), (2, 1000, 8), (1, 0, 4)])
+@pytest.mark.parametrize("B,P,G", [(5, 300, 4), (40, 64, 4), (64, 300, 4), (70, 20, 4), (2, 1000, 8), (1, 0, 4)])
 def test_bf16_decode_small(B, P, G):
     Hkv = 2
     shp = shape(d_model=512, n_heads=G * Hkv, n_kv_heads=Hkv, head_dim=128, d_ff=768,
