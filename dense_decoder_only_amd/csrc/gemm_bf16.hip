@@ -248,6 +248,9 @@ gemm_bf16_kernel(GemmArgs args) {
         // with a scheduling barrier.
         constexpr int NM = TMB * TNB, NR = TMB + TNB;
         constexpr int KS = BK / KSTEP;
+        // the copies ride on k-steps 0..KS-2 (a tile of one k-step, 16x16x32
+        // MFMAs at BK 32, computed wrong results when tried: not supported)
+        static_assert(KS > 1, "interleaved schedules need at least two k-steps per k-tile");
         static_assert(NR <= NM, "reads ride on the MFMAs");
         bf16x8 fa[2][TMB], fb[2][TNB];
         uint32_t a_off[KS], b_off[KS];
@@ -309,7 +312,7 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
         for (int n = 0; n < NR; ++n) rd(0, 0, 0, n);
         // copies per step of 0..KS-2 (the last step carries none)
-        constexpr int CPS = KS > 1 ? (L + KS - 2) / (KS - 1) : L;
+        constexpr int CPS = (L + KS - 2) / (KS - 1);
         constexpr int HALF = NM / 2;
         // The body is the same for every k-tile: near the end, the copies of
         // "k-tile t+STAGES-1" repeat the last k-tile into the free stage and
@@ -333,10 +336,6 @@ gemm_bf16_kernel(GemmArgs args) {
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-            if constexpr (KS == 1) {
-#pragma unroll
-                for (int i = 0; i < L; ++i) dma_one(t_copy, st_copy, i);
             }
             if constexpr (PF_DIST > 0) prefetch(min(t + PF_DIST, nk - 1));
             constexpr int LB = (KS - 1) & 1;  // fragment buffer of the last step
