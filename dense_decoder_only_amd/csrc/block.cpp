@@ -233,10 +233,14 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 //  - 256x256 tiles once they fill at least 160 compute units (gate/up on the
 //    16x16x32 prefetching kernel, the rest on the 8-wave kernel);
 //  - 256x128 tiles (interleaved, BK 64, 3 stages) from 192 tiles up when K is
-//    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that.
+//    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that;
+//  - operands past 4 GiB (beyond the interleaved kernels' 32-bit offsets): the
+//    plain 8-wave or 256x128 / 128x128 kernels.
 int pick_tile(int M, int N, int K, int epi) {
     const int pm = (M + 255) / 256;
     const bool scaled = epi == llb::EPI_QKV || epi == llb::EPI_SWIGLU;
+    if (!llb::gemm_bf16_offsets_fit(M, N, K))  // beyond the interleaved schedules' reach
+        return N % 256 == 0 ? 0 : N % 128 != 0 ? -1 : M > 128 ? 1 : 2;
     if (N % 256 == 0 && M >= 4096) return scaled ? 10 : (K >= 16384 || N >= 32768) ? 4 : 0;
     if (N % 128 != 0) return -1;
     if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 13 : 6;
@@ -266,7 +270,7 @@ int tail_split(const llb_block* b, int cfg, const llb::GemmArgs& a) {
     int tbm, tbn;
     llb::gemm_bf16_tile(kTailCfg, &tbm, &tbn, &nt);
     if (bn != 256 || bm != tbm || a.epi.kind == llb::EPI_RESID_NORM ||
-        !llb::gemm_bf16_supports(kTailCfg, a.N, a.K, a.epi.kind))
+        !llb::gemm_bf16_supports(kTailCfg, a.M, a.N, a.K, a.epi.kind))
         return 0;
     const long pm = (a.M + bm - 1) / bm;
     const long tiles = pm * (a.N / bn);
@@ -393,7 +397,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
             {tile_gu, 2 * c.d_ff, d, llb::EPI_SWIGLU, "gate/up projection"},
             {tile_down, d, c.d_ff, llb::EPI_RESID, "down projection"}};
         for (const auto& k : chk)
-            if (!llb::gemm_bf16_supports(k.cfg, k.N, k.K, k.epi))
+            if (!llb::gemm_bf16_supports(k.cfg, M, k.N, k.K, k.epi))
                 return fail(LLB_E_UNSUPPORTED, "%s: tile configuration %d does not fit N=%d K=%d", k.what,
                             k.cfg, k.N, k.K);
     }
@@ -492,7 +496,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         if (small_m) {
             const int parts = rows_down > 0 ? d / rows_down : llb::gemv_bf16_ssq_parts(d);
             if (parts <= qkv_max_parts(M)) out_parts = parts;
-        } else if (llb::gemm_bf16_supports(tile_down, d, c.d_ff, llb::EPI_RESID_NORM)) {
+        } else if (llb::gemm_bf16_supports(tile_down, M, d, c.d_ff, llb::EPI_RESID_NORM)) {
             int bm, bn, nt;
             llb::gemm_bf16_tile(tile_down, &bm, &bn, &nt);
             out_parts = d / bn;
@@ -1050,7 +1054,7 @@ llb_status llb_model_forward(llb_model* m, const int32_t* tokens, int32_t B, int
         e = llb::gemv_bf16_launch(g, llb::gemv_bf16_splits(R, m->vocab, d), (float*)(w + p.scratch), s);
     } else {
         const int tile = pick_tile(R, m->vocab, d, llb::EPI_LOGITS);
-        if (!llb::gemm_bf16_supports(tile, m->vocab, d, llb::EPI_LOGITS))
+        if (!llb::gemm_bf16_supports(tile, R, m->vocab, d, llb::EPI_LOGITS))
             return fail(LLB_E_UNSUPPORTED, "LM head: no tile fits vocab=%d", m->vocab);
         e = llb::gemm_bf16_launch(g, tile, s);
     }

@@ -104,6 +104,16 @@ LLB_DEV void dma16(const void* gptr, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// The same copy with a scalar base: lane i's 16 bytes come from sbase + voff
+// (voff a per-lane 32-bit byte offset, sbase uniform), so a loop that moves
+// the base by a uniform amount per step needs no per-lane address arithmetic.
+LLB_DEV void dma16_s(uint32_t voff, const void* sbase, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+
 // Four bytes per lane from gptr into LDS at lds + 4 * lane (one 256-byte
 // block per wave), counted by vmcnt like dma16.
 LLB_DEV void dma4(const void* gptr, uint32_t lds) {

@@ -265,28 +265,33 @@ gemm_bf16_kernel(GemmArgs args) {
         }
         constexpr uint32_t STAGE_BYTES = STAGE_ELEMS * 2;
         typedef bf16x8 __attribute__((address_space(3))) * lds_frag_ptr;
-        // (the swizzle of row r + MB i equals that of r: MB i / 2 is a multiple of 8)
-        auto rd_a = [&](int st, int kk, int fbuf, int i) {
-            fa[fbuf][i] = *(lds_frag_ptr)(uintptr_t)(a_off[kk] + st * STAGE_BYTES + i * MB * BK * 2);
-        };
-        auto rd_b = [&](int st, int kk, int fbuf, int j) {
-            fb[fbuf][j] = *(lds_frag_ptr)(uintptr_t)(b_off[kk] + st * STAGE_BYTES + j * MB * BK * 2);
-        };
-        // n-th of the NR fragment reads, in the order the MFMAs (i-major) first
-        // use them: A0 B0 .. B(TNB-1) A1 .. A(TMB-1)
-        auto rd = [&](int st, int kk, int fbuf, int n) {
-            if (n == 0) rd_a(st, kk, fbuf, 0);
-            else if (n <= TNB) rd_b(st, kk, fbuf, n - 1);
-            else rd_a(st, kk, fbuf, n - TNB);
+        // n-th of the NR fragment reads of one k-step, in the order the MFMAs
+        // (i-major) first use them: A0 B0 .. B(TNB-1) A1 .. A(TMB-1).  ab / bb:
+        // that k-step's fragment-0 addresses in the stage (the swizzle of row
+        // r + MB i equals that of r: MB i / 2 is a multiple of 8).
+        auto rd = [&](uint32_t ab, uint32_t bb, int fbuf, int n) {
+            if (n == 0) fa[fbuf][0] = *(lds_frag_ptr)(uintptr_t)(ab);
+            else if (n <= TNB) fb[fbuf][n - 1] = *(lds_frag_ptr)(uintptr_t)(bb + (n - 1) * MB * BK * 2);
+            else fa[fbuf][n - TNB] = *(lds_frag_ptr)(uintptr_t)(ab + (n - TNB) * MB * BK * 2);
         };
         auto mf = [&](int fbuf, int n) {  // n-th of the NM MFMAs of a k-step
             const int i = n / TNB, j = n % TNB;
             if constexpr (M16) acc16[i][j] = mfma16(fa[fbuf][i], fb[fbuf][j], acc16[i][j]);
             else acc[i][j] = mfma32(fa[fbuf][i], fb[fbuf][j], acc[i][j]);
         };
+        // Copies with a scalar base per operand and k-tile and a fixed per-lane
+        // offset: copy i moves A rows for i < NA, W rows after (BM/RPB rows
+        // blocks of A are a multiple of the wave count).
+        constexpr int NA = BM / (RPB * NW);
+        static_assert(BM % (RPB * NW) == 0, "copy i is all-A or all-W");
+        uint32_t voff[L];
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            voff[i] = (uint32_t)((const char*)src[i] - (const char*)(i < NA ? A : W));
         auto dma_one = [&](int kt, int st, int i) {
             const int blk = wave + i * NW;
-            dma16(src[i] + k_off(i, kt), lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
+            const char* sb = i < NA ? (const char*)A + (size_t)kt * BK * 2 : (const char*)W + k_off(NA, kt) * 2;
+            dma16_s(voff[i], sb, lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
         };
         // L2 prefetch (SCHED_INTERLEAVE_PF): each lane touches one 128-byte line
         // of the k-tile PF_DIST ahead of the copies, in one of this wave's 64 A
@@ -310,7 +315,7 @@ gemm_bf16_kernel(GemmArgs args) {
         wait_vm_lgkm<(STAGES - 2) * L>();
         barrier();
 #pragma unroll
-        for (int n = 0; n < NR; ++n) rd(0, 0, 0, n);
+        for (int n = 0; n < NR; ++n) rd(a_off[0], b_off[0], 0, n);
         // copies per step of 0..KS-2 (the last step carries none)
         constexpr int CPS = (L + KS - 2) / (KS - 1);
         constexpr int HALF = NM / 2;
@@ -321,6 +326,16 @@ gemm_bf16_kernel(GemmArgs args) {
             const int t_copy = min(t + STAGES - 1, nk - 1);
             const int st_copy = (st + STAGES - 1) % STAGES;
             const int st_next = (st + 1) % STAGES;
+            // fragment-0 addresses of this tile's k-steps 1..KS-1 and of the
+            // next tile's step 0 (each block's read adds an immediate offset)
+            uint32_t ab[KS], bb[KS];
+#pragma unroll
+            for (int kk = 1; kk < KS; ++kk) {
+                ab[kk] = a_off[kk] + st * STAGE_BYTES;
+                bb[kk] = b_off[kk] + st * STAGE_BYTES;
+            }
+            const uint32_t ab_next = a_off[0] + st_next * STAGE_BYTES;
+            const uint32_t bb_next = b_off[0] + st_next * STAGE_BYTES;
 #pragma unroll
             for (int ks = 0; ks + 1 < KS; ++ks) {
                 // ops of this step: NR reads, then copies ks*CPS .. ks*CPS+CPS-1
@@ -331,7 +346,7 @@ gemm_bf16_kernel(GemmArgs args) {
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int q = n * Q / NM; q < (n + 1) * Q / NM; ++q) {
-                        if (q < NR) rd(st, ks + 1, (ks + 1) & 1, q);
+                        if (q < NR) rd(ab[ks + 1], bb[ks + 1], (ks + 1) & 1, q);
                         else if (ks * CPS + q - NR < L) dma_one(t_copy, st_copy, ks * CPS + q - NR);
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -356,7 +371,7 @@ gemm_bf16_kernel(GemmArgs args) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int q = (n - HALF) * NR / (NM - HALF); q < (n - HALF + 1) * NR / (NM - HALF); ++q)
-                    rd(st_next, 0, 0, q);
+                    rd(ab_next, bb_next, 0, q);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -565,6 +580,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 
 int gemm_bf16_num_tile_cfgs() { return kNumTiles; }
 
+bool gemm_bf16_offsets_fit(long M, long N, long K) {
+    return M * K * 2 <= 0xffffffffL && N * K * 2 <= 0xffffffffL;
+}
+
 hipError_t tile_weights_launch(const void* src, void* dst, int N, int K, hipStream_t s) {
     if (N <= 0 || K <= 0 || N % 128 != 0 || K % 64 != 0 || src == dst) return hipErrorInvalidValue;
     const long units = (long)N * K / 8;
@@ -573,10 +592,12 @@ hipError_t tile_weights_launch(const void* src, void* dst, int N, int K, hipStre
     return hipGetLastError();
 }
 
-bool gemm_bf16_supports(int cfg, int N, int K, int epi) {
+bool gemm_bf16_supports(int cfg, int M, int N, int K, int epi) {
     if (cfg < 0 || cfg >= kNumTiles) return false;
     const TileCfg t = kTiles[cfg];
-    if (N <= 0 || N % t.bn != 0 || K < t.bk || K % t.bk != 0) return false;
+    if (M <= 0 || N <= 0 || N % t.bn != 0 || K < t.bk || K % t.bk != 0) return false;
+    // the interleaved schedules address A and W by 32-bit byte offsets
+    if (t.sched != SCHED_PLAIN && !gemm_bf16_offsets_fit(M, N, K)) return false;
     const int wtn = t.bn / t.wn;
     if (epi == EPI_SWIGLU && wtn % 64 != 0) return false;
     if (epi == EPI_RESID_NORM && wtn != 64 && wtn != 128) return false;
@@ -591,7 +612,7 @@ void gemm_bf16_tile(int cfg, int* bm, int* bn, int* threads) {
 
 hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
     if (cfg < 0 || cfg >= kNumTiles) return hipErrorInvalidValue;
-    if (a.M <= 0 || !gemm_bf16_supports(cfg, a.N, a.K, a.epi.kind)) return hipErrorInvalidValue;
+    if (!gemm_bf16_supports(cfg, a.M, a.N, a.K, a.epi.kind)) return hipErrorInvalidValue;
     const int n_end = a.n_end ? a.n_end : a.N;
     const int bn = kTiles[cfg].bn;
     if (a.n_begin < 0 || a.n_begin % bn != 0 || n_end % bn != 0 || n_end > a.N || a.n_begin >= n_end)

@@ -70,8 +70,11 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int tile_cfg, hipStream_t s);
 // Tile configurations available to gemm_bf16_launch: returns BM, BN, threads.
 // Whether tile configuration cfg can run C[M, N] = A[M, K] W^T with epilogue
 // kind epi (BN divides N, BK divides K, the per-wave column slice holds the
-// epilogue's column groups).
-bool gemm_bf16_supports(int cfg, int N, int K, int epi);
+// epilogue's column groups; the interleaved configurations also need
+// gemm_bf16_offsets_fit).
+bool gemm_bf16_supports(int cfg, int M, int N, int K, int epi);
+// Whether every byte offset into A [M, K] and W [N, K] (bf16) fits 32 bits.
+bool gemm_bf16_offsets_fit(long M, long N, long K);
 void gemm_bf16_tile(int tile_cfg, int* bm, int* bn, int* threads);
 int gemm_bf16_num_tile_cfgs();
 // The bf16 projections read W in 128-row x 64-column tiles: element (n, k) of
