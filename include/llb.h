@@ -240,7 +240,10 @@ llb_status llb_model_forward(llb_model* m, const int32_t* tokens, int32_t B, int
  * [-1, count) give LLB_E_INVALID and change nothing.  A call whose
  * configuration for some projection has a BN that does not divide that
  * projection's N, or a per-wave column slice that cannot hold its fused
- * epilogue, fails with LLB_E_UNSUPPORTED before any work is queued. */
+ * epilogue, or (the interleaved configurations, which address their operands
+ * by 32-bit byte offsets) an operand of 4 GiB or more, fails with
+ * LLB_E_UNSUPPORTED before any work is queued.  The automatic choice falls
+ * back to the plain configurations for such operands. */
 int32_t llb_gemm_num_tiles(void);
 llb_status llb_gemm_tile_info(int32_t cfg, int32_t* bm, int32_t* bn);
 llb_status llb_block_set_tiles(llb_block* blk, int32_t qkv, int32_t o, int32_t gate_up, int32_t down);
