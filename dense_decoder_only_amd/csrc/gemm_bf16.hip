@@ -459,6 +459,10 @@ gemm_bf16_kernel(GemmArgs args) {
             const int rbase = wm * WTM + i * 16;
             float4 sc4 = make_float4(1.f, 1.f, 1.f, 1.f);
             if constexpr (SCALED) sc4 = *(const float4*)&sScale[rbase + 4 * (lane >> 4)];
+            // unscaled epilogues still multiply by an (opaque) 1: staging the
+            // accumulators by plain copies let the register allocator shuffle
+            // them through the main loop (three AGPR moves per MFMA)
+            else asm volatile("" : "+v"(sc4.x), "+v"(sc4.y), "+v"(sc4.z), "+v"(sc4.w));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int rr = 4 * (lane >> 4) + r;
