@@ -242,10 +242,10 @@ int pick_tile(int M, int N, int K, int epi) {
     const bool scaled = epi == llb::EPI_QKV || epi == llb::EPI_SWIGLU;
     if (!llb::gemm_bf16_offsets_fit(M, N, K))  // beyond the interleaved schedules' reach
         return N % 256 == 0 ? 0 : N % 128 != 0 ? -1 : M > 128 ? 1 : 2;
-    if (N % 256 == 0 && M >= 4096) return (scaled || K >= 16384) ? 10 : N >= 32768 ? 4 : 0;
+    if (N % 256 == 0 && M >= 4096) return (scaled || K >= 16384) ? 14 : N >= 32768 ? 4 : 0;
     if (N % 128 != 0) return -1;
-    if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 13 : 6;
-    if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 10 : 0;
+    if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 15 : 6;
+    if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 14 : 0;
     const long t128 = (long)pm * (N / 128);
     if (t128 >= 192 && K % 64 == 0) return 7;
     return M > 128 ? 1 : 2;

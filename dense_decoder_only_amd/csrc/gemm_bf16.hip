@@ -50,7 +50,7 @@ LLB_DEV int swz(int r) {
 // 16x16x32 MFMAs, which do the same work at a lower power draw (more clock
 // under the chip's power limit, measured on random operands).
 constexpr int SCHED_PLAIN = 0, SCHED_INTERLEAVE = 1, SCHED_INTERLEAVE_PF = 2, SCHED_I16 = 3,
-              SCHED_I16_PF = 4;
+              SCHED_I16_PF = 4, SCHED_SPREAD = 8;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OCC, int EPI, int SCHED>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(OCC)))
@@ -67,9 +67,16 @@ gemm_bf16_kernel(GemmArgs args) {
     constexpr int L = BLOCKS / NW;            // DMA instructions per wave per stage
     static_assert(BLOCKS % NW == 0 && BM % RPB == 0, "DMA split");
     static_assert((STAGES - 2) * L < 64, "vmcnt range");
-    constexpr bool INTERLEAVED = SCHED != SCHED_PLAIN;
-    constexpr bool M16 = SCHED == SCHED_I16 || SCHED == SCHED_I16_PF;   // 16x16x32 MFMAs
-    constexpr int PF_DIST = (SCHED == SCHED_INTERLEAVE_PF || SCHED == SCHED_I16_PF) ? 2 : 0;  // in k-tiles
+    constexpr int BASE = SCHED & 7;
+    constexpr bool INTERLEAVED = BASE != SCHED_PLAIN;
+    constexpr bool M16 = BASE == SCHED_I16 || BASE == SCHED_I16_PF;   // 16x16x32 MFMAs
+    constexpr int PF_DIST = (BASE == SCHED_INTERLEAVE_PF || BASE == SCHED_I16_PF) ? 2 : 0;  // in k-tiles
+    // SCHED_SPREAD: a k-tile's copies start in the second half of the last
+    // k-step two k-tiles earlier (the stage is free from that barrier on) and
+    // continue through the first k-step one k-tile earlier, so that the CU's
+    // copy path (about 1 KB per 16 cycles) is never asked for a k-tile's 64 KB
+    // within a quarter of a k-tile.
+    constexpr bool SPREAD = (SCHED & SCHED_SPREAD) != 0;
     constexpr int MB = M16 ? 16 : 32;          // MFMA block edge
     constexpr int KSTEP = M16 ? 32 : 16;       // k per MFMA
     constexpr int TMB = WTM / MB, TNB = WTN / MB;
@@ -312,12 +319,18 @@ gemm_bf16_kernel(GemmArgs args) {
         // keep the count): k-tile 0 landed once (STAGES-2) L copies are pending
         for (int t = nk; t < STAGES - 1; ++t)
             for (int i = 0; i < L; ++i) dma_one(nk - 1, t, i);
-        wait_vm_lgkm<(STAGES - 2) * L>();
+        // SPREAD: the first CA copies of k-tile STAGES-1, as the second half of
+        // a previous k-tile would have issued them
+        constexpr int CA = SPREAD ? (L * 3) / 8 : 0;
+        static_assert(!SPREAD || (KS == 2 && STAGES == 2), "spread copies: two k-steps, two stages");
+        if constexpr (SPREAD)
+            for (int i = 0; i < CA; ++i) dma_one(min(STAGES - 1, nk - 1), STAGES - 1, i);
+        wait_vm_lgkm<(STAGES - 2) * L + CA>();
         barrier();
 #pragma unroll
         for (int n = 0; n < NR; ++n) rd(a_off[0], b_off[0], 0, n);
         // copies per step of 0..KS-2 (the last step carries none)
-        constexpr int CPS = (L + KS - 2) / (KS - 1);
+        constexpr int CPS = SPREAD ? L - CA : (L + KS - 2) / (KS - 1);
         constexpr int HALF = NM / 2;
         // The body is the same for every k-tile: near the end, the copies of
         // "k-tile t+STAGES-1" repeat the last k-tile into the free stage and
@@ -339,6 +352,7 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
             for (int ks = 0; ks + 1 < KS; ++ks) {
                 // ops of this step: NR reads, then copies ks*CPS .. ks*CPS+CPS-1
+                // (SPREAD: reads and the remaining copies CA.. alternate)
                 constexpr int Q = NR + CPS;
 #pragma unroll
                 for (int n = 0; n < NM; ++n) {
@@ -346,8 +360,16 @@ gemm_bf16_kernel(GemmArgs args) {
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int q = n * Q / NM; q < (n + 1) * Q / NM; ++q) {
-                        if (q < NR) rd(ab[ks + 1], bb[ks + 1], (ks + 1) & 1, q);
-                        else if (ks * CPS + q - NR < L) dma_one(t_copy, st_copy, ks * CPS + q - NR);
+                        if constexpr (SPREAD) {
+                            // op q: a copy when q is odd and copies remain, else a read
+                            const int nc = q < 2 * CPS ? (q + 1) / 2 : CPS;   // copies among ops < q+1
+                            const bool is_copy = q < 2 * CPS ? (q & 1) : false;
+                            if (is_copy) dma_one(t_copy, st_copy, CA + nc - 1);
+                            else rd(ab[ks + 1], bb[ks + 1], (ks + 1) & 1, q - nc);
+                        } else {
+                            if (q < NR) rd(ab[ks + 1], bb[ks + 1], (ks + 1) & 1, q);
+                            else if (ks * CPS + q - NR < L) dma_one(t_copy, st_copy, ks * CPS + q - NR);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -365,13 +387,18 @@ gemm_bf16_kernel(GemmArgs args) {
             wait_vm_lgkm<(STAGES - 2) * L + NPF>();
             barrier();
             // last step, second half, with step 0's fragments of k-tile t+1
+            // (SPREAD: then the first CA copies of k-tile t+2 into this stage)
+            constexpr int Q2 = NR + CA;
+            const int t_copy2 = min(t + 2, nk - 1);
 #pragma unroll
             for (int n = HALF; n < NM; ++n) {
                 mf(LB, n);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int q = (n - HALF) * NR / (NM - HALF); q < (n - HALF + 1) * NR / (NM - HALF); ++q)
-                    rd(ab_next, bb_next, 0, q);
+                for (int q = (n - HALF) * Q2 / (NM - HALF); q < (n - HALF + 1) * Q2 / (NM - HALF); ++q) {
+                    if (q < NR) rd(ab_next, bb_next, 0, q);
+                    else dma_one(t_copy2, st, q - NR);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -548,6 +575,8 @@ constexpr TileCfg kTiles[] = {
     {256, 128, 2, 2, 64, 3, 1, 3},  // 7 on 16x16x32 MFMAs
     {256, 192, 2, 2, 64, 2, 1, 3},  // 6 on 16x16x32 MFMAs
     {256, 192, 2, 2, 64, 2, 1, 4},  // 12 with the L2 prefetch
+    {256, 256, 2, 2, 64, 2, 1, 4 + 8},  // 10 with spread copies
+    {256, 192, 2, 2, 64, 2, 1, 4 + 8},  // 13 with spread copies
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -635,7 +664,9 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
         case 10: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
         case 11: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_I16>(a, s);
         case 12: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16>(a, s);
-        default: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
+        case 13: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
+        case 14: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD>(a, s);
+        default: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD>(a, s);
     }
 }
 
