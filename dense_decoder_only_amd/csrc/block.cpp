@@ -225,14 +225,14 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 // (steady clocks):
 //  - long inputs (M >= 4096): 256x256 tiles; for the normalised-operand
 //    projections (QKV, gate/up) and long K (the down projection) the
-//    interleaved kernel on 16x16x32 MFMAs with the L2 prefetch, for the others
-//    the interleaved 32x32x16 kernel with the prefetch at large N and the
-//    8-wave kernel otherwise;
+//    interleaved kernel on 16x16x32 MFMAs with the L2 prefetch and spread
+//    copies, for the others the interleaved 32x32x16 kernel with the
+//    prefetch at large N and the 8-wave kernel otherwise;
 //  - 256x192 tiles when they fill whole rounds of the 256 compute units (the
-//    QKV projection on the 16x16x32 prefetching kernel, others on the
-//    interleaved 32x32x16 kernel);
+//    QKV projection on the 16x16x32 prefetching spread-copy kernel, others on
+//    the interleaved 32x32x16 kernel);
 //  - 256x256 tiles once they fill at least 160 compute units (gate/up on the
-//    16x16x32 prefetching kernel, the rest on the 8-wave kernel);
+//    16x16x32 prefetching spread-copy kernel, the rest on the 8-wave kernel);
 //  - 256x128 tiles (interleaved, BK 64, 3 stages) from 192 tiles up when K is
 //    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that;
 //  - operands past 4 GiB (beyond the interleaved kernels' 32-bit offsets): the
