@@ -321,7 +321,7 @@ gemm_bf16_kernel(GemmArgs args) {
             for (int i = 0; i < L; ++i) dma_one(nk - 1, t, i);
         // SPREAD: the first CA copies of k-tile STAGES-1, as the second half of
         // a previous k-tile would have issued them
-        constexpr int CA = SPREAD ? (L * 3) / 8 : 0;
+        constexpr int CA = SPREAD ? L / 4 : 0;
         static_assert(!SPREAD || (KS == 2 && STAGES == 2), "spread copies: two k-steps, two stages");
         if constexpr (SPREAD)
             for (int i = 0; i < CA; ++i) dma_one(min(STAGES - 1, nk - 1), STAGES - 1, i);
