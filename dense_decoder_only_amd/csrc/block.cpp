@@ -233,7 +233,8 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 //    the interleaved 32x32x16 kernel);
 //  - 256x256 tiles once they fill at least 160 compute units (gate/up on the
 //    16x16x32 prefetching spread-copy kernel, the rest on the 8-wave kernel);
-//  - 256x128 tiles (interleaved, BK 64, 3 stages) from 192 tiles up when K is
+//  - 256x128 tiles (interleaved, BK 64, 3 stages; spread copies for the
+//    residual-only epilogue, the down projection) from 192 tiles up when K is
 //    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that;
 //  - operands past 4 GiB (beyond the interleaved kernels' 32-bit offsets): the
 //    plain 8-wave or 256x128 / 128x128 kernels.
@@ -247,7 +248,7 @@ int pick_tile(int M, int N, int K, int epi) {
     if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 15 : 6;
     if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 14 : 0;
     const long t128 = (long)pm * (N / 128);
-    if (t128 >= 192 && K % 64 == 0) return 7;
+    if (t128 >= 192 && K % 64 == 0) return epi == llb::EPI_RESID ? 16 : 7;
     return M > 128 ? 1 : 2;
 }
 

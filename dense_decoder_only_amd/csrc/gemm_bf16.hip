@@ -322,7 +322,7 @@ gemm_bf16_kernel(GemmArgs args) {
         // SPREAD: the first CA copies of k-tile STAGES-1, as the second half of
         // a previous k-tile would have issued them
         constexpr int CA = SPREAD ? L / 4 : 0;
-        static_assert(!SPREAD || (KS == 2 && STAGES == 2), "spread copies: two k-steps, two stages");
+        static_assert(!SPREAD || KS >= 2, "spread copies: two or more k-steps");
         if constexpr (SPREAD)
             for (int i = 0; i < CA; ++i) dma_one(min(STAGES - 1, nk - 1), STAGES - 1, i);
         wait_vm_lgkm<(STAGES - 2) * L + CA>();
@@ -330,7 +330,7 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
         for (int n = 0; n < NR; ++n) rd(a_off[0], b_off[0], 0, n);
         // copies per step of 0..KS-2 (the last step carries none)
-        constexpr int CPS = SPREAD ? L - CA : (L + KS - 2) / (KS - 1);
+        constexpr int CPS = (L - CA + KS - 2) / (KS - 1);
         constexpr int HALF = NM / 2;
         // The body is the same for every k-tile: near the end, the copies of
         // "k-tile t+STAGES-1" repeat the last k-tile into the free stage and
@@ -364,8 +364,12 @@ gemm_bf16_kernel(GemmArgs args) {
                             // op q: a copy when q is odd and copies remain, else a read
                             const int nc = q < 2 * CPS ? (q + 1) / 2 : CPS;   // copies among ops < q+1
                             const bool is_copy = q < 2 * CPS ? (q & 1) : false;
-                            if (is_copy) dma_one(t_copy, st_copy, CA + nc - 1);
-                            else rd(ab[ks + 1], bb[ks + 1], (ks + 1) & 1, q - nc);
+                            const int ci = CA + ks * CPS + nc - 1;
+                            if (is_copy) {
+                                if (ci < L) dma_one(t_copy, st_copy, ci);
+                            } else {
+                                rd(ab[ks + 1], bb[ks + 1], (ks + 1) & 1, q - nc);
+                            }
                         } else {
                             if (q < NR) rd(ab[ks + 1], bb[ks + 1], (ks + 1) & 1, q);
                             else if (ks * CPS + q - NR < L) dma_one(t_copy, st_copy, ks * CPS + q - NR);
@@ -389,7 +393,7 @@ gemm_bf16_kernel(GemmArgs args) {
             // last step, second half, with step 0's fragments of k-tile t+1
             // (SPREAD: then the first CA copies of k-tile t+2 into this stage)
             constexpr int Q2 = NR + CA;
-            const int t_copy2 = min(t + 2, nk - 1);
+            const int t_copy2 = min(t + STAGES, nk - 1);
 #pragma unroll
             for (int n = HALF; n < NM; ++n) {
                 mf(LB, n);
@@ -577,6 +581,7 @@ constexpr TileCfg kTiles[] = {
     {256, 192, 2, 2, 64, 2, 1, 4},  // 12 with the L2 prefetch
     {256, 256, 2, 2, 64, 2, 1, 4 + 8},  // 10 with spread copies
     {256, 192, 2, 2, 64, 2, 1, 4 + 8},  // 13 with spread copies
+    {256, 128, 2, 2, 64, 3, 1, 1 + 8},  // 7 with spread copies
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -666,7 +671,8 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
         case 12: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16>(a, s);
         case 13: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
         case 14: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD>(a, s);
-        default: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD>(a, s);
+        case 15: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD>(a, s);
+        default: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_INTERLEAVE + SCHED_SPREAD>(a, s);
     }
 }
 

@@ -109,7 +109,7 @@ def test_bf16_prefill_small(d, H, Hkv, dff, B, T, scaled):
 TILE_SHAPE = dict(d_model=1536, n_heads=16, n_kv_heads=4, head_dim=128, d_ff=768)
 
 
-@pytest.mark.parametrize("cfg", range(16))
+@pytest.mark.parametrize("cfg", range(20))
 def test_bf16_prefill_every_tile_config(cfg):
     from dense_decoder_only_amd import llb
     n = llb.llb_gemm_num_tiles()
