@@ -257,9 +257,9 @@ int tile_for(const llb_block* b, int override_cfg, int M, int N, int K, int epi)
     return override_cfg >= 0 ? override_cfg : pick_tile(M, N, K, epi);
 }
 
-// The 256x128 interleaved configuration that takes over a projection's last,
-// partly filled round of 256-wide tiles.
-constexpr int kTailCfg = 7;
+// The 256x128 interleaved configuration (spread copies) that takes over a
+// projection's last, partly filled round of 256-wide tiles.
+constexpr int kTailCfg = 16;
 
 // First output column of the tail of C[M, N] = A W^T under configuration cfg:
 // when 256-wide tiles fill r >= 1 whole rounds of the compute units and leave
