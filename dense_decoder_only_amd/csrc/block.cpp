@@ -10,7 +10,9 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <unordered_set>
 #include <vector>
 
 #include "kernels.h"
@@ -20,7 +22,34 @@ namespace {
 thread_local std::string g_err;
 
 constexpr uint64_t kMagic = 0x4b434f4c42424c4cull;  // "LLBBLOCK"
-constexpr uint64_t kDead = 0xdeadbeefdeadbeefull;
+
+// Live handles.  Every entry point looks a handle up here before reading
+// through it, so a pointer that was never returned by a create call, or whose
+// destroy has already run, is rejected without being dereferenced.
+struct Registry {
+    std::mutex mu;
+    std::unordered_set<const void*> blocks, models;
+};
+Registry& registry() {
+    static Registry r;
+    return r;
+}
+void register_live(std::unordered_set<const void*> Registry::*set, const void* h) {
+    Registry& r = registry();
+    std::lock_guard<std::mutex> lk(r.mu);
+    (r.*set).insert(h);
+}
+bool is_live(std::unordered_set<const void*> Registry::*set, const void* h) {
+    Registry& r = registry();
+    std::lock_guard<std::mutex> lk(r.mu);
+    return (r.*set).count(h) != 0;
+}
+// Removes h; false when it was not live.
+bool unregister_live(std::unordered_set<const void*> Registry::*set, const void* h) {
+    Registry& r = registry();
+    std::lock_guard<std::mutex> lk(r.mu);
+    return (r.*set).erase(h) == 1;
+}
 
 llb_status fail(llb_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 llb_status fail(llb_status st, const char* fmt, ...) {
@@ -67,7 +96,9 @@ struct llb_block {
 
 namespace {
 
-bool handle_ok(const llb_block* b) { return b != nullptr && b->magic == kMagic; }
+bool handle_ok(const llb_block* b) {
+    return b != nullptr && is_live(&Registry::blocks, b) && b->magic == kMagic;
+}
 
 llb_status check_config(const llb_config* c) {
     if (!c) return fail(LLB_E_INVALID, "config is NULL");
@@ -95,7 +126,9 @@ llb_status check_config(const llb_config* c) {
         return fail(LLB_E_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
     if (c->wdtype == LLB_BF16) {
         if (c->head_dim != 128) return fail(LLB_E_UNSUPPORTED, "bf16 blocks need head_dim 128");
-        if (G > 8) return fail(LLB_E_UNSUPPORTED, "bf16 blocks need n_heads / n_kv_heads <= 8");
+        // the bf16 attention kernels hold a query-head group of 1, 2, 4 or 8 per KV head
+        if (G != 1 && G != 2 && G != 4 && G != 8)
+            return fail(LLB_E_UNSUPPORTED, "bf16 blocks need n_heads / n_kv_heads in {1, 2, 4, 8} (got %d)", G);
         if (c->d_model % 256 != 0 || c->d_ff % 256 != 0 || c->n_heads % 2 != 0)
             return fail(LLB_E_UNSUPPORTED,
                         "bf16 blocks need d_model, d_ff multiples of 256 and even n_heads");
@@ -356,9 +389,13 @@ int qkv_max_parts(int M) { return 4 * (M <= 32 ? 32 : 16); }
 //   h = x + Wo . Attn(RMSNorm(x)),  y = h + Wdown . SwiGLU(RMSNorm(h)).
 // pos_host: per-sequence start positions (host, B entries; T = 1), or null:
 // every sequence starts at pos0.  With them, pos0 is their maximum.
+// check_only: run every argument check and return before anything is queued.
+// events: record the stage-timing events when the handle has timing enabled
+// (false: never, so that the call creates no events).
 llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int pos0, void* kc,
                      void* vc, int cap, void* ws, size_t ws_bytes, hipStream_t s, bool decode,
-                     const int32_t* pos_host = nullptr, NormChain* chain = nullptr) {
+                     const int32_t* pos_host = nullptr, NormChain* chain = nullptr,
+                     bool check_only = false, bool events = true) {
     const llb_config& c = b->cfg;
     const int L = pos0 + T;
     const WsPlan p = plan_ws(b, B, T, decode, L);
@@ -404,6 +441,10 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
                             k.cfg, k.N, k.K);
     }
 
+    if (check_only) return LLB_OK;
+    // stage-timing events (none when the caller asked for a call that creates nothing)
+    auto mark = [&]() -> hipError_t { return events ? stage_event(b, s) : hipSuccess; };
+
     const int* pos_b = nullptr;
     if (pos_host) {
         // the positions travel to the workspace in kernel arguments, ahead of the
@@ -418,7 +459,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     e.T = T; e.pos0 = pos0; e.cap = cap; e.n_heads = c.n_heads; e.n_kv = c.n_kv_heads; e.hd = hd;
     e.pos_b = pos_b;
 
-    hipError_t te = stage_event(b, s);
+    hipError_t te = mark();
     if (te != hipSuccess) return hip_fail(te, "stage timing");
 
     // 1. RMSNorm(x) . Wqkv^T, RoPE, Q -> workspace, K/V -> cache rows pos0..pos0+T-1
@@ -437,7 +478,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     a.epi = e; a.epi.kind = llb::EPI_QKV; a.epi.q_out = q; a.epi.k_cache = kc; a.epi.v_cache = vc;
     llb_status st = run_proj(b, a, small_m, scratch, tile_qkv, b->tile_qkv < 0, s, "qkv projection", rows_qkv);
     if (st != LLB_OK) return st;
-    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+    if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
 
     // 2. attention over cache rows 0..pos0+t
     llb::AttnArgs at{};
@@ -449,7 +490,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     else if (decode) he = llb::attn_decode_bf16_launch(at, scratch, s);
     else he = llb::attn_prefill_bf16_launch(at, s);
     if (he != hipSuccess) return hip_fail(he, "attention");
-    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+    if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
 
     // 3. h = x + O . Wo^T   (bf16: also the FFN RMSNorm's operand and row sums of h^2)
     a = llb::GemmArgs{};
@@ -472,7 +513,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     }
     st = run_proj(b, a, small_m, scratch, tile_o, b->tile_o < 0, s, "output projection", rows_o);
     if (st != LLB_OK) return st;
-    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+    if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
 
     // 4. u = SiLU(RMSNorm(h) . Wgate^T) * (RMSNorm(h) . Wup^T)
     a = llb::GemmArgs{};
@@ -485,7 +526,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
     st = run_proj(b, a, small_m, scratch, tile_gu, b->tile_gu < 0, s, "gate/up projection", rows_gu);
     if (st != LLB_OK) return st;
-    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+    if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
 
     // 5. y = h + u . Wdown^T
     a = llb::GemmArgs{};
@@ -511,7 +552,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     st = run_proj(b, a, small_m, scratch, tile_down, b->tile_down < 0, s, "down projection", rows_down);
     if (st != LLB_OK) return st;
     if (chain) chain->out_parts = out_parts;
-    if ((te = stage_event(b, s)) != hipSuccess) return hip_fail(te, "stage timing");
+    if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
     return LLB_OK;
 }
 
@@ -655,16 +696,17 @@ llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* s
         return hip_fail(e, "weight upload");
     }
     b->magic = kMagic;
+    register_live(&Registry::blocks, b);
     *out = b;
     return LLB_OK;
 }
 
 llb_status llb_block_destroy(llb_block* b) {
     if (!b) return LLB_OK;
-    if (b->magic != kMagic) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!unregister_live(&Registry::blocks, b)) return fail(LLB_E_INVALID, "not a live block handle");
     (void)hipDeviceSynchronize();
     free_block(b);
-    b->magic = kDead;
+    b->magic = 0;
     delete b;
     return LLB_OK;
 }
@@ -677,6 +719,19 @@ size_t llb_block_workspace_bytes(const llb_block* b, int32_t B, int32_t T) {
         if (dn > n) n = dn;
     }
     return n;
+}
+
+llb_status llb_block_workspace_layout(const llb_block* b, int32_t B, int32_t T, int32_t decode,
+                                      size_t* offsets) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!offsets) return fail(LLB_E_INVALID, "offsets is NULL");
+    if (B <= 0 || T <= 0 || (decode && T != 1)) return fail(LLB_E_INVALID, "bad sizes");
+    const WsPlan p = plan_ws(b, B, T, decode != 0, T);
+    offsets[0] = p.q;
+    offsets[1] = p.o;
+    offsets[2] = p.h;
+    offsets[3] = p.u;
+    return LLB_OK;
 }
 
 static llb_status check_call(const llb_block* b, const void* x, const void* y, int B, int T,
@@ -893,9 +948,11 @@ struct llb_model {
     void* head;    // [vocab, d] bf16, 128 x 64 tiled layout
 };
 
-static constexpr uint32_t kModelMagic = 0x4c4c4d44u, kModelDead = 0x44454144u;
+static constexpr uint32_t kModelMagic = 0x4c4c4d44u;
 
-static bool model_ok(const llb_model* m) { return m != nullptr && m->magic == kModelMagic; }
+static bool model_ok(const llb_model* m) {
+    return m != nullptr && is_live(&Registry::models, m) && m->magic == kModelMagic;
+}
 
 static void free_model(llb_model* m) {
     for (llb_block* b : m->layers) llb_block_destroy(b);
@@ -954,16 +1011,17 @@ llb_status llb_model_create(const llb_config* cfg, int32_t n_layers, int32_t voc
         return hip_fail(e, "model weight upload");
     }
     m->magic = kModelMagic;
+    register_live(&Registry::models, m);
     *out = m;
     return LLB_OK;
 }
 
 llb_status llb_model_destroy(llb_model* m) {
     if (!m) return LLB_OK;
-    if (m->magic != kModelMagic) return fail(LLB_E_INVALID, "not a live model handle");
+    if (!unregister_live(&Registry::models, m)) return fail(LLB_E_INVALID, "not a live model handle");
     (void)hipDeviceSynchronize();
     free_model(m);
-    m->magic = kModelDead;
+    m->magic = 0;
     delete m;
     return LLB_OK;
 }
@@ -1018,14 +1076,26 @@ llb_status llb_model_forward(llb_model* m, const int32_t* tokens, int32_t B, int
     const bool lo = last_only != 0;
     const ModelWs p = plan_model_ws(m, B, T, lo);
     if (ws_bytes < p.total) return fail(LLB_E_INVALID, "workspace too small: %zu < %zu bytes", ws_bytes, p.total);
+    const int d = m->cfg.d_model, M = B * T;
+    const int R = (lo && T > 1) ? B : M;  // rows the LM head scores
+    // the head's kernel choice, checked before anything is queued
+    const int head_tile = R <= 64 ? -1 : pick_tile(R, m->vocab, d, llb::EPI_LOGITS);
+    if (R > 64 && !llb::gemm_bf16_supports(head_tile, R, m->vocab, d, llb::EPI_LOGITS))
+        return fail(LLB_E_UNSUPPORTED, "LM head: no tile fits vocab=%d", m->vocab);
     hipStream_t s = (hipStream_t)stream;
     char* w = (char*)ws;
     float* x = (float*)(w + p.x);
-    const int d = m->cfg.d_model, M = B * T;
+    if (m->n_layers > 0) {
+        NormChain ch{0, m->n_layers > 1 ? m->layers[1]->g1 : nullptr, 0};
+        const llb_status st = run_block(m->layers[0], x, x, B, T, start_pos, k_caches[0], v_caches[0],
+                                        cache_cap, w + p.blk, p.blk_bytes, s, T == 1, nullptr, &ch, true);
+        if (st != LLB_OK) return st;
+    }
     hipError_t e = llb::embed_launch(tokens, m->embed, x, M, d, m->vocab, s);
     if (e != hipSuccess) return hip_fail(e, "embedding");
     // the blocks, in place on x, each handing the next one its attention RMSNorm
-    // (positions and buffers were checked above)
+    // (positions and buffers were checked above; every layer has the shape and
+    // kernel choices of layer 0, whose call is checked before anything is queued)
     int parts = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         NormChain ch{parts, l + 1 < m->n_layers ? m->layers[l + 1]->g1 : nullptr, 0};
@@ -1035,12 +1105,10 @@ llb_status llb_model_forward(llb_model* m, const int32_t* tokens, int32_t B, int
         parts = ch.out_parts;
     }
     const float* src = x;
-    int R = M;
-    if (lo && T > 1) {
+    if (R != M) {
         e = llb::last_rows_launch(x, (float*)(w + p.xl), B, T, d, s);
         if (e != hipSuccess) return hip_fail(e, "last rows");
         src = (const float*)(w + p.xl);
-        R = B;
     }
     // final RMSNorm operand (bf16 x * g and fp32 sum of squares), then the head
     // with the row's 1/rms in its epilogue
@@ -1055,10 +1123,7 @@ llb_status llb_model_forward(llb_model* m, const int32_t* tokens, int32_t B, int
     if (R <= 64) {
         e = llb::gemv_bf16_launch(g, llb::gemv_bf16_splits(R, m->vocab, d), (float*)(w + p.scratch), s);
     } else {
-        const int tile = pick_tile(R, m->vocab, d, llb::EPI_LOGITS);
-        if (!llb::gemm_bf16_supports(tile, R, m->vocab, d, llb::EPI_LOGITS))
-            return fail(LLB_E_UNSUPPORTED, "LM head: no tile fits vocab=%d", m->vocab);
-        e = llb::gemm_bf16_launch(g, tile, s);
+        e = llb::gemm_bf16_launch(g, head_tile, s);
     }
     if (e != hipSuccess) return hip_fail(e, "LM head");
     return LLB_OK;

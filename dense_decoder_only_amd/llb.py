@@ -34,7 +34,7 @@ EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes"
             "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
             "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles", "llb_block_set_decode_kernels",
             "llb_model_create", "llb_model_destroy", "llb_model_workspace_bytes", "llb_model_forward",
-            "llb_last_error")
+            "llb_block_workspace_layout", "llb_last_error")
 
 STAGES = ("qkv", "attention", "o_proj", "gate_up", "down")
 
@@ -119,6 +119,8 @@ def load_library(path: str = LIB_PATH):
     lib.llb_model_forward.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, vp,
                                       vp, sz, vp]
     lib.llb_model_forward.restype = ctypes.c_int
+    lib.llb_block_workspace_layout.argtypes = [vp, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.llb_block_workspace_layout.restype = ctypes.c_int
     lib.llb_last_error.argtypes = []
     lib.llb_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -338,6 +340,17 @@ def llb_block_stage_times(blk: Block):
     n = ctypes.c_int32()
     _check(load_library().llb_block_stage_times(blk.handle, ms, ctypes.byref(n)), "llb_block_stage_times")
     return dict(zip(STAGES, [float(v) for v in ms])), int(n.value)
+
+
+WS_REGIONS = ("q", "o", "h", "u")
+
+
+def llb_block_workspace_layout(blk: Block, B: int, T: int, decode: bool) -> Dict[str, int]:
+    """Byte offsets of the intermediate results Q, O, h, u in a call's workspace."""
+    offs = (ctypes.c_size_t * 4)()
+    _check(load_library().llb_block_workspace_layout(blk.handle, B, T, 1 if decode else 0, offs),
+           "llb_block_workspace_layout")
+    return dict(zip(WS_REGIONS, [int(v) for v in offs]))
 
 
 def workspace(blk: Block, B: int, T: int, device="cuda") -> torch.Tensor:

@@ -64,8 +64,9 @@ typedef enum { LLB_F32 = 0, LLB_BF16 = 1 } llb_dtype;
  * use_scaled_rope).  Requirements: n_heads % n_kv_heads == 0,
  * n_heads / n_kv_heads <= 16, head_dim in {64, 128}, d_model and d_ff multiples
  * of 64, max_positions >= 1.  bf16 blocks additionally need head_dim == 128,
- * n_heads / n_kv_heads <= 8, d_model and d_ff multiples of 256 and an even
- * n_heads (LLB_E_UNSUPPORTED otherwise). */
+ * n_heads / n_kv_heads in {1, 2, 4, 8} (the query-head groups the attention
+ * kernels hold), d_model and d_ff multiples of 256 and an even n_heads
+ * (LLB_E_UNSUPPORTED otherwise, from create, before anything is allocated). */
 typedef struct {
     int32_t d_model;          /* residual width d */
     int32_t n_heads;          /* query heads */
@@ -104,12 +105,33 @@ llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* s
                             llb_block** out);
 
 /* Frees the library-owned memory of a handle.  Waits for the device first.
- * NULL is accepted.  A handle that was already destroyed is rejected. */
+ * NULL is accepted.  The library keeps a set of its live handles and checks
+ * every handle argument against it before reading through it: a handle that
+ * was already destroyed, or any other pointer that create did not return,
+ * gives LLB_E_INVALID without being dereferenced (a new handle may later be
+ * created at the address of a destroyed one; that address is then live again). */
 llb_status llb_block_destroy(llb_block* blk);
 
 /* Bytes of device workspace that llb_block_prefill (B sequences of T tokens)
  * and, when T == 1, llb_block_decode need.  0 on a bad handle or size. */
 size_t llb_block_workspace_bytes(const llb_block* blk, int32_t B, int32_t T);
+
+/* Test and inspection hook: byte offsets, within the workspace of a call over
+ * B sequences of T new tokens (a decode call when decode != 0, which needs
+ * T == 1), of the intermediate results that call leaves there once it has run:
+ *   offsets[0]  rotated queries Q [B, n_heads, T, head_dim] (wdtype), the output
+ *               of the QKV projection's RoPE ("How Llama 3.1 Generates the Next
+ *               Token", section "RoPE");
+ *   offsets[1]  attention output O [B*T, n_heads*head_dim] (wdtype), heads as
+ *               contiguous column slices ("Llama 3.1 70B", "Grouped-Query
+ *               Attention");
+ *   offsets[2]  h = x + O Wo^T [B*T, d_model] fp32 ("Llama 3.1 70B", "Residual add");
+ *   offsets[3]  u = SiLU(gate) * up [B*T, d_ff] (wdtype) ("Llama 3.1 70B",
+ *               "SwiGLU MLP").
+ * The same call on another stream may overwrite them; they are valid until the
+ * next call that uses the workspace. */
+llb_status llb_block_workspace_layout(const llb_block* blk, int32_t B, int32_t T, int32_t decode,
+                                      size_t* offsets);
 
 /* Prefill: T new tokens per sequence at positions 0..T-1 over an empty cache
  * ("Llama 3.1 70B", "Transformer layer" and "Grouped-Query Attention": causal
@@ -157,8 +179,12 @@ llb_status llb_block_decode_ragged(llb_block* blk, const float* x, float* y, int
                                    int32_t cache_cap, void* ws, size_t ws_bytes, void* stream);
 
 /* Copies k_new, v_new [B, n_kv_heads, n_new, head_dim] (wdtype) into cache
- * rows start_pos..start_pos+n_new-1 of every sequence and KV head.  Used to
- * seed caches.  Needs start_pos + n_new <= cache_cap. */
+ * rows start_pos..start_pos+n_new-1 of every sequence and KV head: the cache
+ * update of "Llama 3 8B - Prepare Q, K, V" ("Explanation" and the model.py
+ * excerpt: the keys and values of the positions being processed are stored in
+ * the cache at their positions, at n_kv_heads, keys already rotated), for
+ * keys and values computed elsewhere (for example to seed a cache).  Needs
+ * start_pos + n_new <= cache_cap; a bad size fails before anything is queued. */
 llb_status llb_kv_append(const llb_block* blk, void* k_cache, void* v_cache, int32_t B,
                          int32_t cache_cap, int32_t start_pos, int32_t n_new,
                          const void* k_new, const void* v_new, void* stream);

@@ -72,6 +72,9 @@ def _create(cfg, weights_ok=True):
     (dict(n_heads=64, n_kv_heads=2), llb.LLB_E_UNSUPPORTED),   # group of 32
     (dict(wdtype=llb.LLB_BF16), llb.LLB_E_UNSUPPORTED),        # bf16 needs head_dim 128
     (dict(wdtype=llb.LLB_BF16, head_dim=128, n_heads=16, n_kv_heads=1), llb.LLB_E_UNSUPPORTED),
+    # bf16 query-head groups outside {1, 2, 4, 8}: no attention kernel holds them
+    (dict(wdtype=llb.LLB_BF16, head_dim=128, n_heads=12, n_kv_heads=4), llb.LLB_E_UNSUPPORTED),   # G = 3
+    (dict(wdtype=llb.LLB_BF16, head_dim=128, n_heads=24, n_kv_heads=4), llb.LLB_E_UNSUPPORTED),   # G = 6
 ])
 def test_create_rejects_bad_configs(kw, status):
     st, out = _create(_cfg(**kw))
@@ -106,6 +109,32 @@ def test_calls_on_bad_handles_fail_before_any_launch():
     assert lib.llb_block_prefill(ctypes.cast(junk, ctypes.c_void_p), p, p, 1, 1, p, p, 8, p, 1 << 20,
                                  None) == llb.LLB_E_INVALID
     assert lib.llb_block_destroy(ctypes.cast(junk, ctypes.c_void_p)) == llb.LLB_E_INVALID
+
+
+def test_unregistered_handles_are_rejected_without_being_read():
+    """A pointer that create never returned is looked up in the library's set of
+    live handles before anything is read through it: even one whose first bytes
+    hold a live handle's magic number, or one into unmapped memory, fails with
+    LLB_E_INVALID."""
+    lib = llb.load_library()
+    lib.llb_model_destroy.argtypes = [ctypes.c_void_p]
+    p = ctypes.c_void_p(1)
+    forged = (ctypes.c_uint64 * 64)()
+    forged[0] = 0x4b434f4c42424c4c          # the block magic, at the magic's offset
+    fake = ctypes.cast(forged, ctypes.c_void_p)
+    assert lib.llb_block_destroy(fake) == llb.LLB_E_INVALID
+    assert lib.llb_block_prefill(fake, p, p, 1, 1, p, p, 8, p, 1 << 20, None) == llb.LLB_E_INVALID
+    assert lib.llb_block_workspace_bytes(fake, 1, 1) == 0
+    forged_m = (ctypes.c_uint32 * 64)()
+    forged_m[0] = 0x4c4c4d44                # the model magic
+    assert lib.llb_model_destroy(ctypes.cast(forged_m, ctypes.c_void_p)) == llb.LLB_E_INVALID
+    assert lib.llb_model_workspace_bytes(ctypes.cast(forged_m, ctypes.c_void_p), 1, 1, 0) == 0
+    # an address no process maps: a read through it would fault
+    wild = ctypes.c_void_p(0x10)
+    assert lib.llb_block_destroy(wild) == llb.LLB_E_INVALID
+    assert lib.llb_model_destroy(wild) == llb.LLB_E_INVALID
+    offs = (ctypes.c_size_t * 4)()
+    assert lib.llb_block_workspace_layout(wild, 1, 1, 0, offs) == llb.LLB_E_INVALID
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

@@ -156,14 +156,17 @@ def _oracle_decode(q, kc, vc, P):
     return np.stack(out)
 
 
-@pytest.mark.parametrize("G,B,P", [
-    (4, 1, 0), (4, 3, 1), (4, 2, 14), (4, 2, 15), (4, 2, 16), (4, 32, 1000),
-    (8, 2, 4096), (1, 2, 200), (2, 3, 77), (8, 64, 129), (8, 1, 16383),
+@pytest.mark.parametrize("G,B,P,Hkv", [
+    (4, 1, 0, 2), (4, 3, 1, 2), (4, 2, 14, 2), (4, 2, 15, 2), (4, 2, 16, 2), (4, 32, 1000, 2),
+    (8, 2, 4096, 2), (1, 2, 200, 2), (2, 3, 77, 2), (8, 64, 129, 2), (8, 1, 16383, 2),
     # >= 128 (sequence, KV head) units: one workgroup per unit, chunks merged in LDS
-    (4, 64, 300), (2, 64, 17), (1, 128, 40),
+    (4, 64, 300, 2), (2, 64, 17, 2), (1, 128, 40, 2),
+    # the 8B and 70B decode shapes: 8 KV heads, 256 and 512 units, L = P + 1 keys
+    (4, 32, 1000, 8), (8, 64, 4096, 8),
+    # the same kernel at the first fused unit count and at ragged key counts
+    (4, 16, 999, 8), (8, 16, 4095, 8), (8, 64, 0, 8), (4, 32, 1, 8),
 ])
-def test_attention_decode_random(G, B, P):
-    Hkv = 2
+def test_attention_decode_random(G, B, P, Hkv):
     shp, blk, _ = _block(G, Hkv, max_positions=16384)
     try:
         H, hd = shp.n_heads, 128
@@ -174,7 +177,7 @@ def test_attention_decode_random(G, B, P):
         vc = kc.clone()
         kc[:, :, :P + 1] = _rand((B, Hkv, P + 1, hd), gen, 0.6)
         vc[:, :, :P + 1] = _rand((B, Hkv, P + 1, hd), gen)
-        note(f"attn decode G={G} B={B} P={P}")
+        note(f"attn decode G={G} B={B} P={P} Hkv={Hkv} ({B * Hkv} units)")
         o = _run_decode(blk, shp, q, kc, vc, P)
         ref = _oracle_decode(q, kc, vc, P)
         mag = _oracle_decode(q, kc, vc.abs(), P)
@@ -185,51 +188,68 @@ def test_attention_decode_random(G, B, P):
         llb.llb_block_destroy(blk)
 
 
+# (G, B, Hkv): 4 units (the split-over-workgroups form), 256 units of 4 heads and
+# 128 units of 8 heads (one workgroup per unit, the form the 8B and 70B decode run)
+UNIT_SHAPES = [(4, 2, 2), (4, 32, 8), (8, 16, 8)]
+
+
+@pytest.mark.parametrize("G,B,Hkv", UNIT_SHAPES)
 @pytest.mark.parametrize("P", [1, 63, 1000, 4096])
-def test_attention_decode_uniform_scores_give_mean_of_all_keys(P):
+def test_attention_decode_uniform_scores_give_mean_of_all_keys(P, G, B, Hkv):
     """q = 0: every visible key has score 0, so o = mean of the P + 1 values.
     V row 0 carries a large marker: dropping key 0 (or reading one key more)
     changes o[0] by about marker / (P + 1)."""
-    shp, blk, _ = _block(4)
+    shp, blk, _ = _block(G, Hkv)
     try:
-        B, H, hd = 2, shp.n_heads, 128
+        H, hd = shp.n_heads, 128
         cap = workloads.cache_capacity(P + 2)
         q = torch.zeros(B, H, hd, dtype=torch.bfloat16)
-        kc = torch.zeros(B, 2, cap, hd, dtype=torch.bfloat16)
-        vc = torch.zeros(B, 2, cap, hd, dtype=torch.bfloat16)
+        kc = torch.zeros(B, Hkv, cap, hd, dtype=torch.bfloat16)
+        vc = torch.zeros(B, Hkv, cap, hd, dtype=torch.bfloat16)
         vc[:, :, 0, 0] = 256.0          # first key's marker
         vc[:, :, P, 1] = 256.0          # own (newest) key's marker
         vc[:, :, P + 1, 2] = 256.0      # one past the end: must not be read
-        note(f"attn decode uniform P={P}")
+        vc[:, :, P + 2:, 3] = 256.0     # every row after that
+        note(f"attn decode uniform P={P} G={G} B={B} Hkv={Hkv} ({B * Hkv} units)")
         o = _run_decode(blk, shp, q, kc, vc, P).float().view(B, H, hd)
         expect = 256.0 / (P + 1)
         assert torch.allclose(o[:, :, 0], torch.full_like(o[:, :, 0], expect), rtol=8e-3)
         assert torch.allclose(o[:, :, 1], torch.full_like(o[:, :, 1], expect), rtol=8e-3)
         assert torch.all(o[:, :, 2] == 0)
+        assert torch.all(o[:, :, 3] == 0)
+        assert torch.all(o[:, :, 4:] == 0)
     finally:
         llb.llb_block_destroy(blk)
 
 
-@pytest.mark.parametrize("mode", ["prefill", "decode"])
-def test_attention_dominant_key_is_selected(mode):
+@pytest.mark.parametrize("mode,G,B,Hkv,P", [
+    ("prefill", 4, 1, 2, 700), ("decode", 4, 1, 2, 700),
+    # one workgroup per (sequence, KV head): 256 units of 4 heads, 512 of 8
+    ("decode", 4, 32, 8, 1000), ("decode", 8, 64, 8, 4096), ("prefill", 8, 2, 8, 700),
+])
+def test_attention_dominant_key_is_selected(mode, G, B, Hkv, P):
     """One key aligned with the query and 30 units of score above the rest: the
-    output is that key's value row, to bf16 precision."""
-    shp, blk, _ = _block(4)
+    output is that key's value row, to bf16 precision.  The dominant key sits at
+    a different row in each sequence, the last one at row P (the newest key)."""
+    shp, blk, _ = _block(G, Hkv)
     try:
-        B, H, hd, Hkv = 1, shp.n_heads, 128, 2
-        P = 700
+        H, hd = shp.n_heads, 128
         T = 1 if mode == "decode" else 40
         pos0 = P if mode == "decode" else P - T + 1
         cap = workloads.cache_capacity(P + 1)
-        gen = torch.Generator().manual_seed(3)
-        star = 123
+        gen = torch.Generator().manual_seed(3 + B + P)
+        # the dominant row of sequence b: spread over 0..pos0 (the first query's
+        # own position in prefill), the last sequence at the newest visible row
+        stars = [(123 + 37 * b) % (pos0 + 1) for b in range(B)]
+        stars[-1] = pos0
         kc = _rand((B, Hkv, cap, hd), gen, 0.05)
         vc = _rand((B, Hkv, cap, hd), gen)
-        kc[:, :, star, :] = 0
-        kc[:, :, star, 0] = 4.0
+        for b, star in enumerate(stars):
+            kc[b, :, star, :] = 0
+            kc[b, :, star, 0] = 4.0
         q = torch.zeros(B, H, T, hd, dtype=torch.bfloat16)
         q[..., 0] = 30.0 * math.sqrt(hd) / 4.0   # q.k_star / sqrt(hd) = 30
-        note(f"attn dominant key {mode}")
+        note(f"attn dominant key {mode} G={G} B={B} Hkv={Hkv} P={P} ({B * Hkv} units)")
         if mode == "decode":
             o = _run_decode(blk, shp, q[:, :, 0], kc, vc, P).float().view(B, H, hd)
             o = o[:, :, None, :]
@@ -237,9 +257,10 @@ def test_attention_dominant_key_is_selected(mode):
             out = torch.empty(B, T, H * hd, dtype=torch.bfloat16, device="cuda")
             llb.llb_attention_prefill(blk, q.cuda(), kc.cuda(), vc.cuda(), out, B, T, pos0, cap)
             o = out.cpu().float().view(B, T, H, hd).permute(0, 2, 1, 3)
-        for h in range(H):
-            ref = vc[0, h // 4, star].float()
-            assert torch.allclose(o[0, h], ref.expand_as(o[0, h]), atol=2e-2, rtol=1e-2)
+        # ref[b, h] = value row stars[b] of KV head h // G
+        ref = vc[torch.arange(B)[:, None], (torch.arange(H) // G)[None, :],
+                 torch.tensor(stars)[:, None]].float()
+        assert torch.allclose(o, ref[:, :, None, :].expand_as(o), atol=2e-2, rtol=1e-2)
     finally:
         llb.llb_block_destroy(blk)
 
@@ -294,3 +315,28 @@ def test_capacity_and_workspace_errors():
         assert ei.value.status == llb.LLB_E_CAPACITY
     finally:
         llb.llb_block_destroy(blk)
+
+
+def test_double_destroy_is_rejected():
+    """A destroyed handle leaves the library's set of live handles: destroying
+    it again, or calling through it, gives LLB_E_INVALID and reads nothing."""
+    import ctypes
+    shp, blk, _ = _block(4)
+    raw = ctypes.c_void_p(blk.handle.value)
+    llb.llb_block_destroy(blk)
+    lib = llb.load_library()
+    assert lib.llb_block_destroy(raw) == llb.LLB_E_INVALID
+    assert "live" in llb.llb_last_error()
+    assert lib.llb_block_workspace_bytes(raw, 1, 1) == 0
+    with pytest.raises(llb.LlbError) as ei:
+        llb.llb_block_set_tiles(llb.Block(raw.value, None))
+    assert ei.value.status == llb.LLB_E_INVALID
+    # a model handle likewise
+    params, _ = workloads.make_model_weights(shp, 1, 128, 5)
+    dev = [{k: v.cuda() for k, v in params["layers"][0].items()}]
+    m = llb.llb_model_create(llb.make_config(shp, 64), dev, 128, params["embed"].cuda(),
+                             params["final_norm"].cuda(), params["lm_head"].cuda())
+    mraw = ctypes.c_void_p(m.handle.value)
+    llb.llb_model_destroy(m)
+    assert lib.llb_model_destroy(mraw) == llb.LLB_E_INVALID
+    assert lib.llb_model_workspace_bytes(mraw, 1, 1, 0) == 0

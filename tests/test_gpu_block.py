@@ -109,12 +109,18 @@ def test_bf16_prefill_small(d, H, Hkv, dff, B, T, scaled):
 TILE_SHAPE = dict(d_model=1536, n_heads=16, n_kv_heads=4, head_dim=128, d_ff=768)
 
 
-@pytest.mark.parametrize("cfg", range(20))
+def _tile_count():
+    """Entries of the library's prefill tile table (0 when it is not built)."""
+    try:
+        from dense_decoder_only_amd import llb
+        return llb.llb_gemm_num_tiles()
+    except Exception:
+        return 0
+
+
+@pytest.mark.parametrize("cfg", range(_tile_count()))
 def test_bf16_prefill_every_tile_config(cfg):
     from dense_decoder_only_amd import llb
-    n = llb.llb_gemm_num_tiles()
-    if cfg >= n:
-        pytest.skip(f"the library has {n} tile configurations")
     bm, bn = llb.llb_gemm_tile_info(cfg)
     shp = shape(**TILE_SHAPE, rope_scaling=False)
     B, T = 1, 300

@@ -210,11 +210,52 @@ def test_llama3_scaling_regimes():
     assert np.array_equal(w[slow], base[slow] / 8.0)
     assert np.all(w[blend] < base[blend]) and np.all(w[blend] > base[blend] / 8.0)
     assert np.all(np.diff(w) < 0)
-    # continuity of the blend at both ends: s -> 1 at lambda = 2048, s -> 0 at 8192
-    for lam0, expect in ((2048.0, 1.0), (8192.0, 1.0 / 8.0)):
-        w0 = 2 * math.pi / lam0
-        s = (8192 / lam0 - 1.0) / 3.0
-        assert ((1 - s) * w0 / 8 + s * w0) / w0 == pytest.approx(expect)
+
+
+@pytest.mark.parametrize("i", [10, 30, 50])
+def test_llama3_blend_is_continuous_at_both_thresholds(i):
+    """The pages fix the two outer regimes (fastest rotations kept, slowest slowed
+    by the factor) but not the blend between them; whatever the blend, it must
+    meet each outer regime where the band begins and ends.  orig_max_pos is set
+    so that pair i's wavelength sits a relative delta inside the band: just
+    above orig/high the oracle's speed must approach omega_i, just below
+    orig/low it must approach omega_i / factor, both to within O(delta).  A
+    blend with its ends swapped, or one that jumps at either threshold, fails."""
+    base = oracle.rope_inv_freq(128, 500000.0)
+    lam = 2 * math.pi / base[i]
+    for delta in (1e-3, 1e-5):
+        near_high = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                         orig_max_pos=4.0 * lam / (1.0 + delta))      # lam = orig/4 * (1 + delta)
+        w = oracle.rope_inv_freq(128, 500000.0, near_high)[i]
+        assert abs(w / base[i] - 1.0) <= 2.0 * delta + 1e-6
+        assert w < base[i]                                             # inside the band: slowed a little
+        near_low = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                        orig_max_pos=lam / (1.0 - delta))             # lam = orig * (1 - delta)
+        w = oracle.rope_inv_freq(128, 500000.0, near_low)[i]
+        assert abs(w / (base[i] / 8.0) - 1.0) <= 3.0 * delta + 1e-6
+        assert w > base[i] / 8.0
+    # just outside the band on either side: exactly the outer regimes
+    out_high = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0, orig_max_pos=4.0 * lam * 1.001)
+    assert oracle.rope_inv_freq(128, 500000.0, out_high)[i] == base[i]
+    out_low = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0, orig_max_pos=lam * 0.999)
+    assert oracle.rope_inv_freq(128, 500000.0, out_low)[i] == np.float32(base[i] / 8.0)
+
+
+def test_llama3_blend_is_monotone_across_the_band():
+    """Sweeping orig_max_pos moves pair i's wavelength through the whole band;
+    the scaled speed must fall monotonically from omega_i to omega_i / factor
+    (a blend in the wrong direction, or non-monotone in the band, fails)."""
+    base = oracle.rope_inv_freq(128, 500000.0)
+    i = 31
+    lam = 2 * math.pi / base[i]
+    ws = []
+    for orig in np.linspace(lam * 1.0001, 4.0 * lam * 0.9999, 200):
+        sc = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0, orig_max_pos=float(orig))
+        ws.append(oracle.rope_inv_freq(128, 500000.0, sc)[i])
+    ws = np.array(ws)
+    # orig grows: the pair moves from the slow end (omega/8) to the fast end (omega)
+    assert np.all(np.diff(ws) >= 0)
+    assert ws[0] < base[i] / 8.0 * 1.001 and ws[-1] > base[i] * 0.999
 
 
 # ----------------------------------------------------------------- attention
