@@ -17,6 +17,10 @@
 
 #include "kernels.h"
 
+// The no-allocation entry point's scratch (see scratch_setup below).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_err;
@@ -67,6 +71,48 @@ llb_status hip_fail(hipError_t e, const char* what) {
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// ---- static scratch of llb_block_decode_noalloc -------------------------------
+// Device memory for callers that cannot allocate: one copy of this array per GPU
+// the library runs on, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the device
+// symbol): llb_block_create looks up each device's copy once, with that device
+// current, and the entry point passes that address to the kernels.
+constexpr int kMaxDevices = 64;
+struct ScratchTable {
+    std::mutex mu;
+    bool looked_up[kMaxDevices] = {};
+    void* ptr[kMaxDevices] = {};
+    hipError_t err[kMaxDevices] = {};
+};
+ScratchTable& scratch_table() {
+    static ScratchTable t;
+    return t;
+}
+
+// Looks up the current device's copy of `scratch` (once per device).
+void scratch_setup(int device) {
+    if (device < 0 || device >= kMaxDevices) return;
+    ScratchTable& t = scratch_table();
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (t.looked_up[device]) return;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    t.looked_up[device] = true;
+    t.err[device] = e;
+    t.ptr[device] = e == hipSuccess ? p : nullptr;
+}
+
+// The device address of `device`'s scratch copy, or null (with the lookup's error).
+void* scratch_ptr(int device, hipError_t* err) {
+    *err = hipErrorInvalidDevice;
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    ScratchTable& t = scratch_table();
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (!t.looked_up[device]) return nullptr;
+    *err = t.err[device];
+    return t.ptr[device];
+}
 
 constexpr double kPi = 3.14159265358979323846;
 
@@ -227,7 +273,7 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
         // (16 columns at the narrowest, token rows padded to 64 in decode)
         p.ssq2 = off; off += align_up(std::max<size_t>(M, 64) * (size_t)(c.d_model / 16) * sizeof(float));
     }
-    size_t scratch = 0;
+    size_t part = 0;
     if (decode && c.wdtype == LLB_BF16) {
         const int d = c.d_model, hq = c.n_heads * c.head_dim;
         const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
@@ -236,19 +282,19 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
             for (auto& s : shapes) {
                 const int sp = llb::gemv_bf16_splits(B, s[0], s[1]);
                 const size_t need = llb::gemv_bf16_ws_bytes(B, s[0], sp);
-                if (need > scratch) scratch = need;
+                if (need > part) part = need;
             }
         }
         const size_t att = llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys);
-        if (att > scratch) scratch = att;
+        if (att > part) part = att;
     }
     if (decode) {  // per-sequence start positions of a ragged decode call
         p.pos = off;
         off += align_up((size_t)B * sizeof(int32_t));
     }
     p.scratch = off;
-    p.scratch_bytes = scratch;
-    off += align_up(scratch);
+    p.scratch_bytes = part;
+    off += align_up(part);
     p.total = off;
     return p;
 }
@@ -341,7 +387,7 @@ int decode_rows(const llb_block* b, int forced, int M, int N, int K, int epi) {
     return 0;
 }
 
-llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, float* scratch,
+llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, float* part,
                     int tile, bool auto_tile, hipStream_t s, const char* what, int rows = 0) {
     hipError_t e;
     if (b->cfg.wdtype == LLB_F32) {
@@ -350,7 +396,7 @@ llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, fl
         e = llb::gemv_narrow_launch(a, rows, b->num_cus, s);
     } else if (small_m) {
         const int sp = llb::gemv_bf16_splits(a.M, a.N, a.K);
-        e = llb::gemv_bf16_launch(a, sp, scratch, s);
+        e = llb::gemv_bf16_launch(a, sp, part, s);
     } else {
         if (tile < 0) return fail(LLB_E_UNSUPPORTED, "%s: no tile fits N=%d", what, a.N);
         const int split = auto_tile ? tail_split(b, tile, a) : 0;
@@ -410,7 +456,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     void* a2 = w + p.a2;
     float* ssq1 = (float*)(w + p.ssq1);
     float* ssq2 = (float*)(w + p.ssq2);
-    float* scratch = (float*)(w + p.scratch);
+    float* part = (float*)(w + p.scratch);
     const int M = B * T;
     const int d = c.d_model, hd = c.head_dim;
     const bool bf16 = c.wdtype == LLB_BF16;
@@ -476,7 +522,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = x; a.gain = b->g1; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_QKV; a.epi.q_out = q; a.epi.k_cache = kc; a.epi.v_cache = vc;
-    llb_status st = run_proj(b, a, small_m, scratch, tile_qkv, b->tile_qkv < 0, s, "qkv projection", rows_qkv);
+    llb_status st = run_proj(b, a, small_m, part, tile_qkv, b->tile_qkv < 0, s, "qkv projection", rows_qkv);
     if (st != LLB_OK) return st;
     if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -487,7 +533,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     at.pos_b = pos_b;
     hipError_t he;
     if (!bf16) he = llb::attn_f32_launch(at, s);
-    else if (decode) he = llb::attn_decode_bf16_launch(at, scratch, s);
+    else if (decode) he = llb::attn_decode_bf16_launch(at, part, s);
     else he = llb::attn_prefill_bf16_launch(at, s);
     if (he != hipSuccess) return hip_fail(he, "attention");
     if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
@@ -511,7 +557,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     } else {
         a.epi.kind = llb::EPI_RESID;
     }
-    st = run_proj(b, a, small_m, scratch, tile_o, b->tile_o < 0, s, "output projection", rows_o);
+    st = run_proj(b, a, small_m, part, tile_o, b->tile_o < 0, s, "output projection", rows_o);
     if (st != LLB_OK) return st;
     if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -524,7 +570,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
         a.A = h; a.gain = b->g2; a.norm = 1;
     }
     a.epi = e; a.epi.kind = llb::EPI_SWIGLU; a.epi.u_out = u;
-    st = run_proj(b, a, small_m, scratch, tile_gu, b->tile_gu < 0, s, "gate/up projection", rows_gu);
+    st = run_proj(b, a, small_m, part, tile_gu, b->tile_gu < 0, s, "gate/up projection", rows_gu);
     if (st != LLB_OK) return st;
     if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
 
@@ -549,7 +595,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
             a.epi.gain = chain->out_gain; a.epi.a_out = a1; a.epi.ssq_out = ssq1;
         }
     }
-    st = run_proj(b, a, small_m, scratch, tile_down, b->tile_down < 0, s, "down projection", rows_down);
+    st = run_proj(b, a, small_m, part, tile_down, b->tile_down < 0, s, "down projection", rows_down);
     if (st != LLB_OK) return st;
     if (chain) chain->out_parts = out_parts;
     if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
@@ -611,6 +657,9 @@ llb_status llb_block_create(const llb_config* cfg, const llb_weights* w, void* s
         delete b;
         return hip_fail(e != hipSuccess ? e : hipErrorInvalidDevice, "compute unit count");
     }
+    // the no-allocation entry point's scratch on this device (its own error is
+    // kept and reported by that entry point)
+    scratch_setup(b->device);
 
     const size_t es = b->es, d = c.d_model, hd = c.head_dim, dff = c.d_ff;
     const size_t nq = (size_t)c.n_heads * hd, nkv = (size_t)c.n_kv_heads * hd;
@@ -803,6 +852,30 @@ llb_status llb_block_decode_ragged(llb_block* b, const float* x, float* y, int32
     }
     return run_block(b, x, y, B, 1, max_pos, k_cache, v_cache, cache_cap, ws, ws_bytes,
                      (hipStream_t)stream, true, start_pos);
+}
+
+llb_status llb_block_decode_noalloc(llb_block* b, const float* x, float* y, int32_t B, int32_t start_pos,
+                                    void* k_cache, void* v_cache, int32_t cache_cap, void* stream) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!x || !y || !k_cache || !v_cache) return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (B <= 0) return fail(LLB_E_INVALID, "B must be positive");
+    if (cache_cap <= 0) return fail(LLB_E_INVALID, "cache_cap must be positive");
+    if (start_pos < 0) return fail(LLB_E_INVALID, "start_pos must be >= 0");
+    if (start_pos + 1 > cache_cap)
+        return fail(LLB_E_CAPACITY, "start_pos+1=%d exceeds cache_cap=%d", start_pos + 1, cache_cap);
+    if (start_pos >= b->cfg.max_positions)
+        return fail(LLB_E_CAPACITY, "start_pos=%d >= max_positions=%d", start_pos, b->cfg.max_positions);
+    const size_t need = plan_ws(b, B, 1, true, start_pos + 1).total;
+    if (need > kScratchBytes)
+        return fail(LLB_E_CAPACITY,
+                    "this call needs %zu bytes of scratch; the static scratch holds %zu (use "
+                    "llb_block_decode with a workspace of llb_block_workspace_bytes bytes)",
+                    need, kScratchBytes);
+    hipError_t se;
+    void* ws = scratch_ptr(b->device, &se);
+    if (!ws) return hip_fail(se, "static scratch lookup");
+    return run_block(b, x, y, B, 1, start_pos, k_cache, v_cache, cache_cap, ws, kScratchBytes,
+                     (hipStream_t)stream, true, nullptr, nullptr, false, /*events=*/false);
 }
 
 llb_status llb_kv_append(const llb_block* b, void* k_cache, void* v_cache, int32_t B,

@@ -34,7 +34,7 @@ EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes"
             "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
             "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles", "llb_block_set_decode_kernels",
             "llb_model_create", "llb_model_destroy", "llb_model_workspace_bytes", "llb_model_forward",
-            "llb_block_workspace_layout", "llb_last_error")
+            "llb_block_workspace_layout", "llb_block_decode_noalloc", "llb_last_error")
 
 STAGES = ("qkv", "attention", "o_proj", "gate_up", "down")
 
@@ -119,6 +119,8 @@ def load_library(path: str = LIB_PATH):
     lib.llb_model_forward.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, vp,
                                       vp, sz, vp]
     lib.llb_model_forward.restype = ctypes.c_int
+    lib.llb_block_decode_noalloc.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, vp]
+    lib.llb_block_decode_noalloc.restype = ctypes.c_int
     lib.llb_block_workspace_layout.argtypes = [vp, i32, i32, i32, ctypes.POINTER(sz)]
     lib.llb_block_workspace_layout.restype = ctypes.c_int
     lib.llb_last_error.argtypes = []
@@ -213,6 +215,13 @@ def llb_block_decode(blk: Block, x, y, B, start_pos, k_cache, v_cache, cache_cap
     _check(load_library().llb_block_decode(blk.handle, _ptr(x), _ptr(y), B, start_pos, _ptr(k_cache),
                                            _ptr(v_cache), cache_cap, _ptr(ws), ws.numel() * ws.element_size(),
                                            _stream(stream)), "llb_block_decode")
+
+
+def llb_block_decode_noalloc(blk: Block, x, y, B, start_pos, k_cache, v_cache, cache_cap, stream=None):
+    """llb_block_decode on the library's static scratch: no workspace argument."""
+    _check(load_library().llb_block_decode_noalloc(blk.handle, _ptr(x), _ptr(y), B, start_pos, _ptr(k_cache),
+                                                   _ptr(v_cache), cache_cap, _stream(stream)),
+           "llb_block_decode_noalloc")
 
 
 def llb_block_decode_ragged(blk: Block, x, y, B, start_pos, k_cache, v_cache, cache_cap, ws, stream=None):

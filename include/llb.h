@@ -178,6 +178,25 @@ llb_status llb_block_decode_ragged(llb_block* blk, const float* x, float* y, int
                                    const int32_t* start_pos, void* k_cache, void* v_cache,
                                    int32_t cache_cap, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory, nor hand the library a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same decode as llb_block_decode (the same kernels and
+ * results, bit for bit), with its workspace taken from a static scratch array
+ * of 64 MiB that the library holds on each GPU it runs on until the process
+ * ends.  It allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine, and it records no timing events (llb_block_set_stage_timing does not
+ * apply).  The caller still passes x, y and the caches.  A call whose workspace
+ * (llb_block_workspace_bytes(blk, B, 1) at its P) exceeds 64 MiB fails with
+ * LLB_E_CAPACITY before anything is queued; for the 8B and 70B shapes it holds
+ * B up to 64 at any P the RoPE table allows.  The array keeps the last call's
+ * contents; no part of it has to start at zero (each call writes everything it
+ * reads).  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (on different streams, or from different threads) race and
+ * must be ordered by the caller.  LLB_E_HIP if the array's device address could
+ * not be looked up when the block was created. */
+llb_status llb_block_decode_noalloc(llb_block* blk, const float* x, float* y, int32_t B, int32_t start_pos,
+                                    void* k_cache, void* v_cache, int32_t cache_cap, void* stream);
+
 /* Copies k_new, v_new [B, n_kv_heads, n_new, head_dim] (wdtype) into cache
  * rows start_pos..start_pos+n_new-1 of every sequence and KV head: the cache
  * update of "Llama 3 8B - Prepare Q, K, V" ("Explanation" and the model.py
