@@ -26,6 +26,7 @@ SOURCES = [
     "attn_decode_bf16.hip",
     "f32_path.hip",
     "model_kernels.hip",
+    "probes.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -942,6 +942,29 @@ llb_status llb_attention_decode(const llb_block* b, const void* q, const void* k
     return LLB_OK;
 }
 
+llb_status llb_probe_hbm_read(const void* src, size_t bytes, int32_t n_workgroups, void* sink, void* stream) {
+    if (!src || !sink) return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (bytes == 0 || bytes % 16 != 0 || n_workgroups <= 0)
+        return fail(LLB_E_INVALID, "bytes must be a positive multiple of 16 and n_workgroups positive");
+    const hipError_t e = llb::probe_read_launch(src, bytes, (uint32_t*)sink, n_workgroups, (hipStream_t)stream);
+    return e == hipSuccess ? LLB_OK : hip_fail(e, "read probe");
+}
+
+llb_status llb_probe_hbm_copy(void* dst, const void* src, size_t bytes, int32_t n_workgroups, void* stream) {
+    if (!src || !dst) return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (bytes == 0 || bytes % 16 != 0 || n_workgroups <= 0)
+        return fail(LLB_E_INVALID, "bytes must be a positive multiple of 16 and n_workgroups positive");
+    const hipError_t e = llb::probe_copy_launch(dst, src, bytes, n_workgroups, (hipStream_t)stream);
+    return e == hipSuccess ? LLB_OK : hip_fail(e, "copy probe");
+}
+
+llb_status llb_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, void* sink, void* stream) {
+    if (!sink) return fail(LLB_E_INVALID, "sink is NULL");
+    if (n_workgroups <= 0 || iters <= 0) return fail(LLB_E_INVALID, "n_workgroups and iters must be positive");
+    const hipError_t e = llb::probe_mfma_launch((float*)sink, n_workgroups, iters, (hipStream_t)stream);
+    return e == hipSuccess ? LLB_OK : hip_fail(e, "MFMA probe");
+}
+
 int32_t llb_gemm_num_tiles(void) { return llb::gemm_bf16_num_tile_cfgs(); }
 
 llb_status llb_gemm_tile_info(int32_t cfg, int32_t* bm, int32_t* bn) {

@@ -137,6 +137,16 @@ hipError_t last_rows_launch(const float* src, float* dst, int B, int T, int d, h
 // dst[0..n) = src[0..n) (src on the host), through kernel arguments: ordered on
 // stream s like the kernels, and src may be reused as soon as this returns.
 hipError_t store_ints_launch(int* dst, const int* src, int n, hipStream_t s);
+// ---- measurement probes (probes.hip) -----------------------------------------
+// Stream `bytes` (a multiple of 16) from src with n_wg workgroups of 256 lanes;
+// sink gets one word per workgroup.
+hipError_t probe_read_launch(const void* src, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s);
+// dst[0..bytes) = src[0..bytes), the same access pattern.
+hipError_t probe_copy_launch(void* dst, const void* src, size_t bytes, int n_wg, hipStream_t s);
+// n_wg workgroups of 4 waves, each wave iters x 8 independent 16x16x32 bf16 MFMAs;
+// sink gets one float per wave (4 n_wg).
+hipError_t probe_mfma_launch(float* sink, int n_wg, int iters, hipStream_t s);
+
 hipError_t kv_append_launch(void* kc, void* vc, const void* kn, const void* vn, int B, int n_kv,
                             int cap, int pos0, int n_new, int hd, int elem_bytes, hipStream_t s);
 

@@ -34,7 +34,8 @@ EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes"
             "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
             "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles", "llb_block_set_decode_kernels",
             "llb_model_create", "llb_model_destroy", "llb_model_workspace_bytes", "llb_model_forward",
-            "llb_block_workspace_layout", "llb_block_decode_noalloc", "llb_last_error")
+            "llb_block_workspace_layout", "llb_block_decode_noalloc", "llb_probe_hbm_read",
+            "llb_probe_hbm_copy", "llb_probe_mfma_bf16", "llb_last_error")
 
 STAGES = ("qkv", "attention", "o_proj", "gate_up", "down")
 
@@ -123,6 +124,12 @@ def load_library(path: str = LIB_PATH):
     lib.llb_block_decode_noalloc.restype = ctypes.c_int
     lib.llb_block_workspace_layout.argtypes = [vp, i32, i32, i32, ctypes.POINTER(sz)]
     lib.llb_block_workspace_layout.restype = ctypes.c_int
+    lib.llb_probe_hbm_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.llb_probe_hbm_read.restype = ctypes.c_int
+    lib.llb_probe_hbm_copy.argtypes = [vp, vp, sz, i32, vp]
+    lib.llb_probe_hbm_copy.restype = ctypes.c_int
+    lib.llb_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+    lib.llb_probe_mfma_bf16.restype = ctypes.c_int
     lib.llb_last_error.argtypes = []
     lib.llb_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -316,6 +323,23 @@ def llb_model_forward(m: Model, tokens, B, T, start_pos, k_caches, v_caches, cac
     _check(load_library().llb_model_forward(m.handle, _ptr(tokens), B, T, start_pos, kc, vc, cache_cap,
                                             1 if last_only else 0, _ptr(logits), _ptr(ws),
                                             ws.numel() * ws.element_size(), _stream(stream)), "llb_model_forward")
+
+
+def llb_probe_hbm_read(src, sink, n_workgroups: int, stream=None) -> None:
+    """Streams src (a contiguous device tensor) once; sink: n_workgroups uint32 words."""
+    _check(load_library().llb_probe_hbm_read(_ptr(src), src.numel() * src.element_size(), n_workgroups,
+                                             _ptr(sink), _stream(stream)), "llb_probe_hbm_read")
+
+
+def llb_probe_hbm_copy(dst, src, n_workgroups: int, stream=None) -> None:
+    _check(load_library().llb_probe_hbm_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
+                                             n_workgroups, _stream(stream)), "llb_probe_hbm_copy")
+
+
+def llb_probe_mfma_bf16(n_workgroups: int, iters: int, sink, stream=None) -> None:
+    """sink: 4 * n_workgroups floats."""
+    _check(load_library().llb_probe_mfma_bf16(n_workgroups, iters, _ptr(sink), _stream(stream)),
+           "llb_probe_mfma_bf16")
 
 
 def llb_gemm_num_tiles() -> int:

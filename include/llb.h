@@ -310,6 +310,25 @@ llb_status llb_block_set_tiles(llb_block* blk, int32_t qkv, int32_t o, int32_t g
 llb_status llb_block_set_decode_kernels(llb_block* blk, int32_t qkv, int32_t o, int32_t gate_up,
                                         int32_t down);
 
+/* ---- Measurement probes ---------------------------------------------------
+ * Not part of the block: instruments that measure, on the GPU in use, the two
+ * rates the block's kernels are bound by, so that roofline fractions can be
+ * given against measured peaks as well as nominal ones.  Each enqueues one
+ * kernel on `stream` (current device) and is timed by the caller.
+ * llb_probe_hbm_read: streams `bytes` (a positive multiple of 16) from src with
+ *   16-byte loads over n_workgroups workgroups of 256 lanes; sink (device) gets
+ *   one uint32 per workgroup.  Bytes moved: `bytes`.
+ * llb_probe_hbm_copy: copies `bytes` from src to dst (non-overlapping) with the
+ *   same pattern.  Bytes moved: 2 * `bytes`.
+ * llb_probe_mfma_bf16: n_workgroups workgroups of 4 waves; each wave issues
+ *   iters x 8 independent 16x16x32 bf16 MFMAs on pseudo-random operands; sink
+ *   (device) gets 4 * n_workgroups floats.  FLOPs: n_workgroups * 4 * iters * 8
+ *   * 16384.
+ * A bad argument gives LLB_E_INVALID before anything is queued. */
+llb_status llb_probe_hbm_read(const void* src, size_t bytes, int32_t n_workgroups, void* sink, void* stream);
+llb_status llb_probe_hbm_copy(void* dst, const void* src, size_t bytes, int32_t n_workgroups, void* stream);
+llb_status llb_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, void* sink, void* stream);
+
 /* Thread-local text describing the last non-OK status ("" if none). */
 const char* llb_last_error(void);
 

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(llb.LIB_PATH),
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(llb_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(llb_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_abi():
