@@ -287,6 +287,9 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
         }
         const size_t att = llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys);
         if (att > part) part = att;
+        // the pieces of a ragged batch's long sequences
+        const size_t rag = llb::attn_decode_parts_ws_bytes(c.n_heads, c.head_dim);
+        if (rag > part) part = rag;
     }
     if (decode) {  // per-sequence start positions of a ragged decode call
         p.pos = off;
@@ -416,6 +419,19 @@ llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, fl
     return LLB_OK;
 }
 
+// bf16 decode attention: a ragged batch (pos_host: the host's start positions)
+// whose lengths are uneven enough runs as balanced parts; everything else one
+// workgroup per (sequence, KV head), or split over workgroups for few units.
+hipError_t attention_decode(const llb_block* b, const llb::AttnArgs& at, const int32_t* pos_host, float* part,
+                            hipStream_t s) {
+    if (pos_host) {
+        bool launched = false;
+        const hipError_t e = llb::attn_decode_ragged_launch(at, pos_host, b->num_cus, part, s, &launched);
+        if (e != hipSuccess || launched) return e;
+    }
+    return llb::attn_decode_bf16_launch(at, part, s);
+}
+
 // Blocks run back to back (a model) hand the attention RMSNorm of the next
 // block to the down projection of this one: its epilogue writes, besides
 // y = h + down, the next block's operand bf16(y * g1') and partial sums of y^2
@@ -514,6 +530,9 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     if (bf16 && chain && chain->in_parts > 0) {
         // the previous block's down projection wrote the operand and the partials
         a.A = a1; a.ssq_in = ssq1; a.ssq_count = chain->in_parts;
+    } else if (bf16 && rows_qkv > 0 && llb::gemv_narrow_norm_supports(M, nqkv, d, rows_qkv, b->num_cus)) {
+        // the narrow decode kernel forms the RMSNorm itself from x and g1
+        a.A = x; a.gain = b->g1; a.norm = 1;
     } else if (bf16) {
         hipError_t ne = llb::norm_rows_launch(x, b->g1, a1, ssq1, M, d, s);
         if (ne != hipSuccess) return hip_fail(ne, "attention RMSNorm");
@@ -533,7 +552,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     at.pos_b = pos_b;
     hipError_t he;
     if (!bf16) he = llb::attn_f32_launch(at, s);
-    else if (decode) he = llb::attn_decode_bf16_launch(at, part, s);
+    else if (decode) he = attention_decode(b, at, pos_host, part, s);
     else he = llb::attn_prefill_bf16_launch(at, s);
     if (he != hipSuccess) return hip_fail(he, "attention");
     if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
@@ -917,8 +936,11 @@ llb_status llb_attention_prefill(const llb_block* b, const void* q, const void* 
 size_t llb_attention_workspace_bytes(const llb_block* b, int32_t B, int32_t n_keys) {
     if (!handle_ok(b) || B <= 0 || n_keys <= 0) return 0;
     const llb_config& c = b->cfg;
-    if (c.wdtype == LLB_F32) return 256;
-    return align_up(llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys));
+    // partials (split form, or the pieces of a ragged batch), then B start positions
+    const size_t pos = align_up((size_t)B * sizeof(int32_t));
+    if (c.wdtype == LLB_F32) return 256 + pos;
+    return align_up(std::max(llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys),
+                             llb::attn_decode_parts_ws_bytes(c.n_heads, c.head_dim))) + pos;
 }
 
 llb_status llb_attention_decode(const llb_block* b, const void* q, const void* k_cache,
@@ -963,6 +985,38 @@ llb_status llb_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, void* sink, 
     if (n_workgroups <= 0 || iters <= 0) return fail(LLB_E_INVALID, "n_workgroups and iters must be positive");
     const hipError_t e = llb::probe_mfma_launch((float*)sink, n_workgroups, iters, (hipStream_t)stream);
     return e == hipSuccess ? LLB_OK : hip_fail(e, "MFMA probe");
+}
+
+llb_status llb_attention_decode_ragged(const llb_block* b, const void* q, const void* k_cache,
+                                       const void* v_cache, void* o, int32_t B, const int32_t* start_pos,
+                                       int32_t cache_cap, void* ws, size_t ws_bytes, void* stream) {
+    if (!handle_ok(b)) return fail(LLB_E_INVALID, "not a live block handle");
+    if (!q || !k_cache || !v_cache || !o || !ws || !start_pos)
+        return fail(LLB_E_INVALID, "a buffer pointer is NULL");
+    if (B <= 0 || cache_cap <= 0) return fail(LLB_E_INVALID, "bad sizes");
+    int max_pos = 0;
+    for (int i = 0; i < B; ++i) {
+        if (start_pos[i] < 0) return fail(LLB_E_INVALID, "start_pos[%d]=%d must be >= 0", i, start_pos[i]);
+        if (start_pos[i] + 1 > cache_cap)
+            return fail(LLB_E_CAPACITY, "start_pos[%d]+1=%d exceeds cache_cap=%d", i, start_pos[i] + 1, cache_cap);
+        max_pos = std::max(max_pos, start_pos[i]);
+    }
+    const size_t need = llb_attention_workspace_bytes(b, B, max_pos + 1);
+    if (ws_bytes < need) return fail(LLB_E_INVALID, "workspace too small: %zu < %zu", ws_bytes, need);
+    const llb_config& c = b->cfg;
+    hipStream_t s = (hipStream_t)stream;
+    llb::AttnArgs at{};
+    at.q = q; at.k_cache = k_cache; at.v_cache = v_cache; at.o = o; at.B = B; at.T = 1;
+    at.pos0 = max_pos; at.cap = cache_cap; at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads;
+    at.hd = c.head_dim;
+    // the positions travel to the end of the workspace in kernel arguments
+    int* pos_dev = (int*)((char*)ws + need - align_up((size_t)B * sizeof(int32_t)));
+    hipError_t e = llb::store_ints_launch(pos_dev, start_pos, B, s);
+    if (e != hipSuccess) return hip_fail(e, "start positions");
+    at.pos_b = pos_dev;
+    e = c.wdtype == LLB_F32 ? llb::attn_f32_launch(at, s) : attention_decode(b, at, start_pos, (float*)ws, s);
+    if (e != hipSuccess) return hip_fail(e, "attention decode");
+    return LLB_OK;
 }
 
 int32_t llb_gemm_num_tiles(void) { return llb::gemm_bf16_num_tile_cfgs(); }

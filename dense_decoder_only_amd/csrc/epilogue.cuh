@@ -37,7 +37,7 @@ LLB_DEV void epi_qkv(const Epilogue& e, int m, int n, float v, float partner) {
     const int Hk = e.n_kv * hd;
     const int b = m / e.T;
     const int t = m - b * e.T;
-    const int pos = (e.pos_b ? e.pos_b[b] : e.pos0) + t;
+    const int pos = seq_start(e, b) + t;
     const int j = n & (hd - 1);
     if (n < Hq + Hk) {
         const float2 cs = e.rope[(size_t)pos * (hd >> 1) + (j >> 1)];
@@ -92,7 +92,7 @@ LLB_DEV void epi_qkv8(const Epilogue& e, int m, int n, float* v) {
     const int Hk = e.n_kv * hd;
     const int b = m / e.T;
     const int t = m - b * e.T;
-    const int pos = (e.pos_b ? e.pos_b[b] : e.pos0) + t;
+    const int pos = seq_start(e, b) + t;
     const int j = n & (hd - 1);
     bf16_t* dst;
     if (n < Hq + Hk) {

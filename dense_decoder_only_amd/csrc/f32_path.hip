@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
     const int hd = a.hd;
     const int G = a.n_heads / a.n_kv;
     const int g = h / G;
-    const int pos = (a.pos_b ? a.pos_b[b] : a.pos0) + t;
+    const int pos = seq_start(a, b) + t;
     const int L = pos + 1;
     const float* q = (const float*)a.q + (((size_t)b * a.n_heads + h) * a.T + t) * hd;
     const size_t head_off = ((size_t)b * a.n_kv + g) * a.cap * hd;

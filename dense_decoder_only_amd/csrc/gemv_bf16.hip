@@ -365,25 +365,41 @@ gemv_reduce_kernel(GemmArgs args, int splits, const float* __restrict__ part) {
 // no partial ever leaves the CU.  RW = 16 uses 16x16x32 MFMAs, RW = 32 the
 // 32x32x16 ones.
 
+// Bytes of one wave's pipeline stage: RW weight rows and the MT token rows of
+// a 64-wide k-tile, as bf16 operands or (NORM) as fp32 rows of x plus the
+// k-tile's 64 RMSNorm gains.
+constexpr int narrow_stage(int rw, int ms, bool norm) {
+    return norm ? (rw / 8 + 32 * ms / 4) * 1024 + 256 : (rw + 32 * ms) * GV_BK * 2;
+}
+
 // Ring depth: as deep as LDS allows, for one workgroup per CU or (TWO) two.
-constexpr int narrow_ns(int rw, int ms, bool two) {
-    const int stage = (rw + 32 * ms) * GV_BK * 2;
-    const int ns = (two ? 75 * 1024 : 150 * 1024) / (4 * stage);
+constexpr int narrow_ns(int rw, int ms, bool two, bool norm = false) {
+    const int ns = (two ? 75 * 1024 : 150 * 1024) / (4 * narrow_stage(rw, ms, norm));
     return ns > 6 ? 6 : ns < 2 ? 2 : ns;
 }
 
-template <int MS, int EPI, int RW, int NS>
+// NORM (EPI_QKV): the attention RMSNorm is formed inside the kernel.  A is the
+// fp32 residual stream x and args.gain its gain: each wave copies the fp32 x
+// rows and the 64 gains of its k-tiles into its ring, and the fragment reads
+// form the operand bf16(x * g) (rounded once, as the separate norm kernel
+// would) while summing x^2 for the row's 1/rms ("Llama 3.1 70B", section
+// "RMSNorm": one fp32 reduction per token).  Each element of a wave's k-range
+// enters exactly one lane's sum; the lanes of a row and then the four waves are
+// added in a fixed order, so the result is deterministic.
+template <int MS, int EPI, int RW, int NS, bool NORM>
 __global__ void __launch_bounds__(256)
 gemv_narrow_kernel(GemmArgs args) {
     constexpr int MT = 32 * MS;
     constexpr int W_BLK = RW / 8;       // 1 KB copy blocks per stage: 8 rows of 128 bytes
-    constexpr int A_BLK = MT / 8;
+    constexpr int A_BLK = NORM ? MT / 4 : MT / 8;   // fp32 rows: 4 per 1 KB block
     constexpr int DPW = W_BLK + A_BLK;  // a wave issues every copy of its stages
-    constexpr int STAGE = DPW * 1024;
+    constexpr int VPS = DPW + (NORM ? 1 : 0);       // vector-memory ops per stage (+ the gains)
+    constexpr int STAGE = narrow_stage(RW, MS, NORM);
     constexpr bool SCALED = EPI == EPI_QKV;
-    constexpr int SL = 4;
+    constexpr int SL = NORM ? 0 : 4;
     static_assert(EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_RESID_NORM, "epilogue");
-    static_assert((NS - 2) * DPW + SL < 64, "vmcnt range");
+    static_assert(!NORM || (EPI == EPI_QKV && MS == 1), "in-kernel RMSNorm: QKV over at most 32 token rows");
+    static_assert((NS - 2) * VPS + SL < 64, "vmcnt range");
     static_assert(MT * RW * 4 <= NS * STAGE, "partial tile fits in a wave's ring");
     __shared__ __attribute__((aligned(1024))) char smem[4 * NS * STAGE];
     __shared__ __attribute__((aligned(16))) float s_part[1024];
@@ -400,31 +416,44 @@ gemv_narrow_kernel(GemmArgs args) {
 
     const bf16_t* __restrict__ W = (const bf16_t*)args.W;
     const bf16_t* __restrict__ A = (const bf16_t*)args.A;
+    const float* __restrict__ X = (const float*)args.A;
     // Copy block i of a stage: LDS rows 8i..8i+7 of [W rows; token rows], lane ->
     // (row 8i + lane/8, LDS chunk lane%8) holding global chunk (lane%8) ^ swz(row).
     // The RW rows of one k-tile are RW * 128 contiguous bytes of the 128 x 64
-    // tiled weight layout.
-    const bf16_t* src[DPW];
+    // tiled weight layout.  NORM: after the W blocks, fp32 token rows of 256
+    // bytes (sixteen 16-byte chunks, chunk c of row r at position c ^ (r & 15)),
+    // 4 rows per block, then the k-tile's 64 gains.
+    const char* src[DPW];
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
-        const int row = i * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ gv_swz(row);
-        if (i < W_BLK)
-            src[i] = W + ((size_t)(n0 >> 7) * nkt + kt0) * 8192 + ((n0 & 127) + row) * 64 + chunk * 8;
-        else
-            src[i] = A + (size_t)min(row - RW, M - 1) * K + (size_t)kt0 * GV_BK + chunk * 8;
+        if (i < W_BLK) {
+            const int row = i * 8 + (lane >> 3);
+            const int chunk = (lane & 7) ^ gv_swz(row);
+            src[i] = (const char*)(W + ((size_t)(n0 >> 7) * nkt + kt0) * 8192 + ((n0 & 127) + row) * 64 + chunk * 8);
+        } else if constexpr (NORM) {
+            const int row = (i - W_BLK) * 4 + (lane >> 4);
+            const int chunk = (lane & 15) ^ (row & 15);
+            src[i] = (const char*)(X + (size_t)min(row, M - 1) * K + (size_t)kt0 * GV_BK + chunk * 4);
+        } else {
+            const int row = i * 8 + (lane >> 3);
+            const int chunk = (lane & 7) ^ gv_swz(row);
+            src[i] = (const char*)(A + (size_t)min(row - RW, M - 1) * K + (size_t)kt0 * GV_BK + chunk * 8);
+        }
     }
+    const float* gsrc = NORM ? args.gain + (size_t)kt0 * GV_BK + lane : nullptr;
     const uint32_t ring = lds_offset(smem) + (uint32_t)wave * NS * STAGE;
     auto issue = [&](int j) {  // k-tile kt0 + j into stage j % NS of this wave's ring
         const uint32_t st = ring + (uint32_t)(j % NS) * STAGE;
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
-            dma16(src[i] + (size_t)j * (i < W_BLK ? 8192 : GV_BK), st + (uint32_t)i * 1024);
+            dma16(src[i] + (size_t)j * (i < W_BLK ? 8192 * 2 : NORM ? GV_BK * 4 : GV_BK * 2),
+                  st + (uint32_t)i * 1024);
+        if constexpr (NORM) dma4(gsrc + (size_t)j * GV_BK, st + (uint32_t)DPW * 1024);
     };
 
-    RowScales<MT, SL> rs;
+    RowScales<MT, SL == 0 ? 1 : SL> rs;
     for (int j = 0; j < NS - 1 && j < nk; ++j) issue(j);
-    if (SCALED) rs.issue(args);
+    if (SCALED && !NORM) rs.issue(args);
 
     constexpr int NACC = RW == 32 ? MS : 2 * MS;
     f32x16 acc32[RW == 32 ? MS : 1];
@@ -440,8 +469,34 @@ gemv_narrow_kernel(GemmArgs args) {
         }
     }
     typedef bf16x8 __attribute__((address_space(3))) * lds_frag_ptr;
+    typedef f32x4 __attribute__((address_space(3))) * lds_f4_ptr;
     auto frag = [&](uint32_t st, int row, int c) {
         return *(lds_frag_ptr)(uintptr_t)(st + row * 128 + ((c ^ gv_swz(row)) << 4));
+    };
+    // token-row operand fragment: row trow (of MT), 8-element chunk c of the
+    // k-tile.  NORM: bf16(x * g) from the staged fp32 row and gains, adding the
+    // eight x^2 to ss.
+    constexpr int NSS = RW == 32 ? MS : 2 * MS;
+    float ss[NSS];
+#pragma unroll
+    for (int i = 0; i < NSS; ++i) ss[i] = 0.f;
+    auto afrag = [&](uint32_t st, int trow, int c, float& acc_ss) -> bf16x8 {
+        if constexpr (NORM) {
+            const uint32_t rb = st + W_BLK * 1024 + trow * 256;
+            const f32x4 x0 = *(lds_f4_ptr)(uintptr_t)(rb + (((2 * c) ^ (trow & 15)) << 4));
+            const f32x4 x1 = *(lds_f4_ptr)(uintptr_t)(rb + (((2 * c + 1) ^ (trow & 15)) << 4));
+            const uint32_t gb = st + DPW * 1024 + c * 32;
+            const f32x4 g0 = *(lds_f4_ptr)(uintptr_t)(gb);
+            const f32x4 g1 = *(lds_f4_ptr)(uintptr_t)(gb + 16);
+            acc_ss += x0[0] * x0[0] + x0[1] * x0[1] + x0[2] * x0[2] + x0[3] * x0[3];
+            acc_ss += x1[0] * x1[0] + x1[1] * x1[1] + x1[2] * x1[2] + x1[3] * x1[3];
+            const float v[8] = {x0[0] * g0[0], x0[1] * g0[1], x0[2] * g0[2], x0[3] * g0[3],
+                                x1[0] * g1[0], x1[1] * g1[1], x1[2] * g1[2], x1[3] * g1[3]};
+            return to_bf16x8(v);
+        } else {
+            (void)acc_ss;
+            return frag(st, RW + trow, c);
+        }
     };
 
     for (int j = 0; j < nk; ++j) {
@@ -449,8 +504,8 @@ gemv_narrow_kernel(GemmArgs args) {
         // (and the row-scale loads, when j was issued before them) are in flight;
         // the wait also retires this wave's LDS reads of the stage refilled next
         const int later = min(NS - 2, nk - 1 - j);
-        if (SCALED && j < NS - 1) wait_later<DPW, SL, NS - 2>(later);
-        else wait_later<DPW, 0, NS - 2>(later);
+        if (SCALED && !NORM && j < NS - 1) wait_later<VPS, SL, NS - 2>(later);
+        else wait_later<VPS, 0, NS - 2>(later);
         if (j + NS - 1 < nk) issue(j + NS - 1);
         const uint32_t st = ring + (uint32_t)(j % NS) * STAGE;
         if constexpr (RW == 32) {
@@ -461,7 +516,7 @@ gemv_narrow_kernel(GemmArgs args) {
                 const bf16x8 wf = frag(st, lane & 31, c);
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms)
-                    acc32[ms] = mfma32(frag(st, RW + ms * 32 + (lane & 31), c), wf, acc32[ms]);
+                    acc32[ms] = mfma32(afrag(st, ms * 32 + (lane & 31), c, ss[ms]), wf, acc32[ms]);
             }
         } else {
             // lane: W row lane%16 / token row lane%16, chunk 4*kk + lane/16
@@ -471,7 +526,7 @@ gemv_narrow_kernel(GemmArgs args) {
                 const bf16x8 wf = frag(st, lane & 15, c);
 #pragma unroll
                 for (int tb = 0; tb < 2 * MS; ++tb)
-                    acc16[tb] = mfma16(frag(st, RW + tb * 16 + (lane & 15), c), wf, acc16[tb]);
+                    acc16[tb] = mfma16(afrag(st, tb * 16 + (lane & 15), c, ss[tb]), wf, acc16[tb]);
             }
         }
     }
@@ -495,8 +550,30 @@ gemv_narrow_kernel(GemmArgs args) {
             for (int r = 0; r < 4; ++r)
                 part[(tb * 16 + 4 * (lane >> 4) + r) * RW + (lane & 15)] = acc16[tb][r];
     }
+    if constexpr (NORM) {
+        // each row's sum of x^2: the lanes holding the row (lane ^ 32 for the
+        // 32-row fragments, lane ^ 16, ^ 32 for the 16-row ones), then the waves
+        // in order
+#pragma unroll
+        for (int i = 0; i < NSS; ++i) {
+            if constexpr (RW == 16) ss[i] += __shfl_xor(ss[i], 16, 64);
+            ss[i] += __shfl_xor(ss[i], 32, 64);
+        }
+        constexpr int RB = RW == 32 ? 32 : 16;   // rows per fragment block
+        if (lane < RB) {
+#pragma unroll
+            for (int i = 0; i < NSS; ++i) s_part[wave * MT + i * RB + lane] = ss[i];
+        }
+    }
     __syncthreads();
-    if (SCALED) rs.finish(args, s_part, sscale);
+    if constexpr (NORM) {
+        if (tid < MT)
+            sscale[tid] = inv_rms(((s_part[tid] + s_part[MT + tid]) + s_part[2 * MT + tid]) + s_part[3 * MT + tid],
+                                  K, args.eps);
+        __syncthreads();
+    } else if (SCALED) {
+        rs.finish(args, s_part, sscale);
+    }
 
     // C[m, n0 + c] for 8 columns c0..c0+7, summed over the waves in order
     const float* p0 = (const float*)smem;
@@ -543,7 +620,15 @@ gemv_narrow_kernel(GemmArgs args) {
 
 template <int MS, int EPI, int RW, bool TWO>
 hipError_t launch_narrow(const GemmArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((gemv_narrow_kernel<MS, EPI, RW, narrow_ns(RW, MS, TWO)>), dim3(a.N / RW),
+    if constexpr (EPI == EPI_QKV && MS == 1 && !TWO) {
+        if (a.norm) {
+            hipLaunchKernelGGL((gemv_narrow_kernel<1, EPI_QKV, RW, narrow_ns(RW, 1, false, true), true>),
+                               dim3(a.N / RW), dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    if (a.norm) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_narrow_kernel<MS, EPI, RW, narrow_ns(RW, MS, TWO), false>), dim3(a.N / RW),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }
@@ -623,9 +708,14 @@ bool gemv_narrow_supports(int M, int N, int K, int epi, int rw) {
            K / GV_BK >= 4 && (epi == EPI_QKV || epi == EPI_RESID || epi == EPI_RESID_NORM);
 }
 
+bool gemv_narrow_norm_supports(int M, int N, int K, int rw, int num_cus) {
+    return gemv_narrow_supports(M, N, K, EPI_QKV, rw) && M <= 32 && N / rw <= num_cus;
+}
+
 hipError_t gemv_narrow_launch(const GemmArgs& a, int rw, int num_cus, hipStream_t s) {
     if (!gemv_narrow_supports(a.M, a.N, a.K, a.epi.kind, rw)) return hipErrorInvalidValue;
-    if (a.epi.kind == EPI_QKV && a.ssq_count > 4 * (a.M <= 32 ? 32 : 16)) return hipErrorInvalidValue;
+    if (a.norm && !gemv_narrow_norm_supports(a.M, a.N, a.K, rw, num_cus)) return hipErrorInvalidValue;
+    if (a.epi.kind == EPI_QKV && !a.norm && a.ssq_count > 4 * (a.M <= 32 ? 32 : 16)) return hipErrorInvalidValue;
     const bool two = a.N / rw > num_cus;  // more workgroups than CUs: two fit per CU
     switch (a.epi.kind) {
         case EPI_QKV: return launch_narrow_epi<EPI_QKV>(a, rw, two, s);

@@ -64,6 +64,12 @@ struct GemmArgs {
     int n_begin, n_end;
 };
 
+// Start position of sequence b (see Epilogue::pos_b).
+template <typename Args>
+__device__ __forceinline__ int seq_start(const Args& e, int b) {
+    return e.pos_b ? e.pos_b[b] : e.pos0;
+}
+
 // ---- bf16 MFMA projections -----------------------------------------------
 // Large-M projection (prefill): LDS-staged bf16 MFMA tiles.
 hipError_t gemm_bf16_launch(const GemmArgs& a, int tile_cfg, hipStream_t s);
@@ -99,6 +105,10 @@ hipError_t gemv_bf16_launch(const GemmArgs& a, int splits, float* ws, hipStream_
 // EPI_RESID_NORM writes N / rw partial sums of squares.  Needs N % 128 == 0 (the
 // tiled weight layout) and K a multiple of 64 with K >= 256.
 bool gemv_narrow_supports(int M, int N, int K, int epi, int rw);
+// The QKV projection with the attention RMSNorm formed inside the narrow kernel
+// (args.norm = 1: A is fp32 x [M, K] and args.gain its gain; no ssq_in): at
+// most 32 token rows and one workgroup per CU (N / rw <= num_cus).
+bool gemv_narrow_norm_supports(int M, int N, int K, int rw, int num_cus);
 hipError_t gemv_narrow_launch(const GemmArgs& a, int rw, int num_cus, hipStream_t s);
 
 // RMSNorm operand: a[m, :] = bf16(x[m, :] * g), ssq[m] = sum_j x[m, j]^2 (fp32).
@@ -123,6 +133,16 @@ hipError_t attn_prefill_bf16_launch(const AttnArgs& a, hipStream_t s);
 // Split-K decode attention + merge.  ws: attn_decode_ws_bytes(...) bytes.
 size_t attn_decode_ws_bytes(int B, int n_heads, int n_kv, int hd, int n_keys);
 hipError_t attn_decode_bf16_launch(const AttnArgs& a, float* ws, hipStream_t s);
+// Decode attention of a ragged batch (sequence b reads keys 0..pos_host[b];
+// pos_host on the host): when the batch has enough (sequence, KV head) units for
+// one workgroup per unit and its longest sequence is well above the mean, the
+// keys are packed into num_cus / n_kv bins of equal size, one workgroup per
+// (bin, KV head); sequences that span bins are merged in order by a second
+// kernel.  *launched tells whether it ran (false: use attn_decode_bf16_launch
+// with a.pos_b).  ws: attn_decode_parts_ws_bytes.
+size_t attn_decode_parts_ws_bytes(int n_heads, int hd);
+hipError_t attn_decode_ragged_launch(const AttnArgs& a, const int* pos_host, int num_cus, float* ws,
+                                     hipStream_t s, bool* launched);
 // Plain fp32 attention (prefill or decode, any T).
 hipError_t attn_f32_launch(const AttnArgs& a, hipStream_t s);
 

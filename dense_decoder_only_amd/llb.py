@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "LLB_OK", -1: "LLB_E_INVALID", -2: "LLB_E_UNSUPPORTED", -3: "
 
 EXPORTED = ("llb_block_create", "llb_block_destroy", "llb_block_workspace_bytes",
             "llb_block_prefill", "llb_block_prefill_at", "llb_block_decode", "llb_block_decode_ragged", "llb_kv_append", "llb_attention_prefill",
-            "llb_attention_decode", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
+            "llb_attention_decode", "llb_attention_decode_ragged", "llb_attention_workspace_bytes", "llb_block_set_stage_timing",
             "llb_block_stage_times", "llb_gemm_num_tiles", "llb_gemm_tile_info", "llb_block_set_tiles", "llb_block_set_decode_kernels",
             "llb_model_create", "llb_model_destroy", "llb_model_workspace_bytes", "llb_model_forward",
             "llb_block_workspace_layout", "llb_block_decode_noalloc", "llb_probe_hbm_read",
@@ -96,6 +96,8 @@ def load_library(path: str = LIB_PATH):
     lib.llb_attention_prefill.restype = ctypes.c_int
     lib.llb_attention_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, sz, vp]
     lib.llb_attention_decode.restype = ctypes.c_int
+    lib.llb_attention_decode_ragged.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.POINTER(i32), i32, vp, sz, vp]
+    lib.llb_attention_decode_ragged.restype = ctypes.c_int
     lib.llb_attention_workspace_bytes.argtypes = [vp, i32, i32]
     lib.llb_attention_workspace_bytes.restype = sz
     lib.llb_block_set_stage_timing.argtypes = [vp, i32]
@@ -264,6 +266,16 @@ def llb_attention_decode(blk: Block, q, k_cache, v_cache, o, B, start_pos, cache
                                                _ptr(o), B, start_pos, cache_cap, _ptr(ws),
                                                ws.numel() * ws.element_size(), _stream(stream)),
            "llb_attention_decode")
+
+
+def llb_attention_decode_ragged(blk: Block, q, k_cache, v_cache, o, B, start_pos, cache_cap, ws, stream=None):
+    """start_pos: B host integers, one position per sequence."""
+    if len(start_pos) != B:
+        raise ValueError("start_pos must have B entries")
+    pos = (ctypes.c_int32 * B)(*[int(p) for p in start_pos])
+    _check(load_library().llb_attention_decode_ragged(blk.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+                                                      B, pos, cache_cap, _ptr(ws), ws.numel() * ws.element_size(),
+                                                      _stream(stream)), "llb_attention_decode_ragged")
 
 
 class Model:

@@ -340,3 +340,97 @@ def test_double_destroy_is_rejected():
     llb.llb_model_destroy(m)
     assert lib.llb_model_destroy(mraw) == llb.LLB_E_INVALID
     assert lib.llb_model_workspace_bytes(mraw, 1, 1, 0) == 0
+
+
+def _run_decode_ragged(blk, shp, q, kc, vc, pos):
+    B = q.shape[0]
+    H, hd = shp.n_heads, 128
+    cap = kc.shape[2]
+    ws = torch.empty(llb.llb_attention_workspace_bytes(blk, B, max(pos) + 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, H * hd, dtype=torch.bfloat16, device="cuda")
+    llb.llb_attention_decode_ragged(blk, q.cuda(), kc.cuda(), vc.cuda(), o, B, pos, cap, ws)
+    return o.cpu()
+
+
+def _spread_positions(B, P):
+    """round((2b + 1) P / B): evenly spread over 0..2P (the ragged decode workload's rule)."""
+    return [int(round((2 * b + 1) * P / B)) for b in range(B)]
+
+
+@pytest.mark.parametrize("G,B,Hkv,kind", [
+    (4, 32, 8, "spread1000"),    # the 8B ragged decode: 31..1969, long sequences cut into pieces
+    (8, 64, 8, "random4096"),    # 70B heads, positions 0..4096 at random
+    (4, 40, 4, "one_long"),      # 160 units, one sequence 20x the others
+    (4, 3, 2, "random300"),      # 6 units: the split-over-workgroups form with per-sequence lengths
+    (2, 64, 2, "equal"),         # equal lengths: balanced already, one workgroup per unit
+])
+def test_attention_decode_ragged(G, B, Hkv, kind):
+    """Query b at its own position P_b reads keys 0..P_b of its sequence: every
+    query against the oracle on its own sequence; cache rows past P_b hold a
+    large sentinel that must never be read."""
+    gen = torch.Generator().manual_seed(5000 + B + G)
+    if kind == "spread1000":
+        pos = _spread_positions(B, 1000)
+    elif kind == "random4096":
+        pos = torch.randint(0, 4097, (B,), generator=gen).tolist()
+        pos[0], pos[1], pos[-1] = 0, 4096, 17
+    elif kind == "one_long":
+        pos = [100] * B
+        pos[7] = 2047
+    elif kind == "random300":
+        pos = [0, 300, 123]
+    else:
+        pos = [500] * B
+    shp, blk, _ = _block(G, Hkv, max_positions=8192)
+    try:
+        H, hd = shp.n_heads, 128
+        cap = workloads.cache_capacity(max(pos) + 2)
+        q = _rand((B, H, hd), gen)
+        kc = torch.full((B, Hkv, cap, hd), SENTINEL, dtype=torch.bfloat16)
+        vc = kc.clone()
+        for b, p in enumerate(pos):
+            kc[b, :, :p + 1] = _rand((Hkv, p + 1, hd), gen, 0.6)
+            vc[b, :, :p + 1] = _rand((Hkv, p + 1, hd), gen)
+        note(f"attn decode ragged {kind} G={G} B={B} Hkv={Hkv} positions {min(pos)}..{max(pos)}")
+        o = _run_decode_ragged(blk, shp, q, kc, vc, pos)
+        worst = 0.0
+        for b, p in enumerate(pos):
+            ref = oracle.attention(q[b][:, None, :], kc[b], vc[b], [p], n_keys=p + 1)[:, 0, :].reshape(-1)
+            mag = oracle.attention(q[b][:, None, :], kc[b], vc[b].abs(), [p], n_keys=p + 1)[:, 0, :].reshape(-1)
+            worst = max(worst, bf16_err(o[b], ref, c=1e-3, mag=mag))
+        note(f"  worst bf16 err {worst:.3f}")
+        assert worst <= 1.0
+    finally:
+        llb.llb_block_destroy(blk)
+
+
+@pytest.mark.parametrize("G,B,Hkv", [(4, 32, 8), (8, 64, 8), (4, 3, 2)])
+def test_attention_decode_ragged_uniform_scores_give_mean_of_own_keys(G, B, Hkv):
+    """q = 0, so query b's output is the mean of its P_b + 1 values.  V carries
+    markers on key 0, on key P_b (the newest) and on key P_b + 1 (one past the
+    end, never read), so a piece boundary that drops or repeats a key, or a
+    piece that reads into the next, moves the result by about marker / (P_b + 1)."""
+    pos = _spread_positions(B, 1000) if B >= 32 else [0, 999, 257]
+    shp, blk, _ = _block(G, Hkv)
+    try:
+        H, hd = shp.n_heads, 128
+        cap = workloads.cache_capacity(max(pos) + 2)
+        q = torch.zeros(B, H, hd, dtype=torch.bfloat16)
+        kc = torch.zeros(B, Hkv, cap, hd, dtype=torch.bfloat16)
+        vc = torch.zeros(B, Hkv, cap, hd, dtype=torch.bfloat16)
+        for b, p in enumerate(pos):
+            vc[b, :, 0, 0] = 256.0
+            vc[b, :, p, 1] = 256.0
+            vc[b, :, p + 1:, 2] = 256.0
+        note(f"attn decode ragged uniform G={G} B={B} Hkv={Hkv}")
+        o = _run_decode_ragged(blk, shp, q, kc, vc, pos).float().view(B, H, hd)
+        for b, p in enumerate(pos):
+            expect = torch.full_like(o[b, :, 0], 256.0 / (p + 1))
+            if p == 0:
+                expect = torch.full_like(o[b, :, 0], 256.0)   # key 0 is the newest: both markers
+            assert torch.allclose(o[b, :, 0], expect, rtol=8e-3), (b, p)
+            assert torch.allclose(o[b, :, 1], torch.full_like(o[b, :, 1], 256.0 / (p + 1)), rtol=8e-3), (b, p)
+            assert torch.all(o[b, :, 2] == 0), (b, p)
+            assert torch.all(o[b, :, 3:] == 0), (b, p)
+    finally:
+        llb.llb_block_destroy(blk)

@@ -1,11 +1,19 @@
 """GPU parity of the model forward (embedding, L blocks, final RMSNorm, LM head)
 against the fp64 oracle, through the C ABI.
 
-Bar on the logits: max|gpu - oracle| / rms(oracle) <= 2e-2 * sqrt(L + 1).  Each
-block's output carries the single-block bf16 error (<= 2e-2 by the same metric,
-the block's bar) into the fp32 trunk; independent per-block errors add in
-quadrature over the L blocks, and the head's bf16 operand adds one more term.
-Layer 0's new cache rows keep the block bar (its input, the embedding, is exact).
+Bar on the logits: max|gpu - oracle| / rms(oracle) <= 1.6e-2 * sqrt(L + 1).
+Measured on MI355X (these seeded inputs, deterministic kernels):
+
+    L = 1  (width 512)                 9.9e-3   -> 7.0e-3 * sqrt(L + 1)
+    L = 2  (width 512; 8B widths)      1.8e-2; 1.4e-2, 1.3e-2
+    L = 3  (width 512)                 2.0e-2, 1.4e-2, 1.8e-2 (chunk), 1.2e-2 (decode)
+    L = 32 (Llama-3.1-8B, 128256 ids)  4.6e-2 (decode, B=32 at P=1000), 3.4e-2 (prefill)
+
+The error grows as sqrt(L + 1) (independent per-block errors in the fp32 trunk,
+the head's operand one more term): the coefficient err / sqrt(L + 1) stays in
+7e-3 .. 1.06e-2 from 1 to 32 layers.  The bar is 1.5x the largest coefficient
+measured.  Layer 0's new cache rows keep the block bar (its input, the
+embedding, is exact).
 """
 import math
 
@@ -22,8 +30,15 @@ pytestmark = pytest.mark.gpu
 SMALL = workloads.BlockShape(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=768)
 
 
+MODEL_COEF = 1.6e-2
+
+
 def _bar(L):
-    return 2e-2 * math.sqrt(L + 1)
+    return MODEL_COEF * math.sqrt(L + 1)
+
+
+# Bar of the 32-layer 8B model's logits (max|gpu - oracle| / rms(oracle)).
+FULL_DEPTH_BAR = _bar(32)
 
 
 class GpuModel:
@@ -181,3 +196,60 @@ def test_model_full_width_8b_layers():
     e_d, e_p = rel_err(dec, ref_d), rel_err(pre, ref_p)
     note(f"  decode {e_d:.2e}  prefill {e_p:.2e}  (bar {_bar(L):.2e})")
     assert e_d <= _bar(L) and e_p <= _bar(L)
+
+
+def test_model_full_depth_8b_decode_as_timed():
+    """The 32-layer Llama-3.1-8B model decode that bench.py times (B = 32
+    sequences at P = 1000 over random caches, last-position logits over 128256
+    ids, every layer's new cache row), checked on 4 of the 32 sequences
+    against the oracle run on those sequences alone (sequences are independent).
+    Also records the error of each layer's new K row, to show how the error
+    grows through the stack."""
+    wl = workloads.get("8b_bf16_model_decode")
+    shp, L, V, B, P = wl.shape, wl.layers, wl.vocab, wl.B, wl.P
+    note("model full depth decode: generating weights and caches")
+    params, gen = workloads.make_model_weights(shp, L, V, wl.seed)
+    cap = workloads.cache_capacity(P + 1)
+    kc, vc = _caches(shp, L, B, P, cap, gen)
+    tok = workloads.make_tokens(B, 1, V, gen)
+    gm = GpuModel(shp, params, cap)
+    try:
+        kd, vd = [k.cuda() for k in kc], [v.cuda() for v in vc]
+        note("model full depth decode: GPU forward")
+        logits = gm.forward(tok, P, kd, vd, True)
+        k_new = [k[:, :, P].cpu() for k in kd]
+        del kd, vd
+    finally:
+        gm.close()
+    sel = [0, 9, 22, 31]
+    note("model full depth decode: oracle on 4 sequences")
+    ref, ks, _ = oracle.model_forward(shp, params, tok[sel], [k[sel] for k in kc], [v[sel] for v in vc], P,
+                                      last_only=True)
+    e = rel_err(logits[sel], ref)
+    e_layers = [bf16_err(k_new[l][sel], ks[l][:, :, 0]) for l in range(L)]
+    note(f"  logits {e:.3e} (bar {FULL_DEPTH_BAR:.1e}); new K rows by layer (bf16 metric): "
+         + " ".join(f"{v:.2f}" for v in e_layers))
+    assert e <= FULL_DEPTH_BAR
+    assert torch.isfinite(logits).all()
+
+
+def test_model_full_depth_8b_prefill_last_logits():
+    """The 32-layer 8B model on a 256-token prefill, last-position logits."""
+    shp, L, V = workloads.LLAMA31_8B, 32, 128256
+    B, T = 1, 256
+    note("model full depth prefill: generating weights")
+    params, gen = workloads.make_model_weights(shp, L, V, 12)
+    cap = workloads.cache_capacity(T)
+    kc, vc = _caches(shp, L, B, 0, cap, gen)
+    tok = workloads.make_tokens(B, T, V, gen)
+    gm = GpuModel(shp, params, cap)
+    try:
+        note("model full depth prefill: GPU forward")
+        logits = gm.forward(tok, 0, [k.cuda() for k in kc], [v.cuda() for v in vc], True)
+    finally:
+        gm.close()
+    note("model full depth prefill: oracle")
+    ref, _, _ = oracle.model_forward(shp, params, tok, kc, vc, 0, last_only=True)
+    e = rel_err(logits, ref)
+    note(f"  logits {e:.3e} (bar {FULL_DEPTH_BAR:.1e})")
+    assert e <= FULL_DEPTH_BAR
