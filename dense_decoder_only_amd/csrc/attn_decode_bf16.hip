@@ -26,32 +26,6 @@ namespace {
 constexpr int AD_TARGET_WAVES = 4096;
 constexpr int AD_FUSED_MIN_UNITS = 128;  // (sequence, KV head) units for the one-workgroup-per-unit form
 
-// Ragged batches (attn_decode_ragged_launch): the keys of all sequences are
-// packed into n_bins bins of near-equal size, one workgroup per (bin, KV head).
-// A bin holds consecutive segments; a segment is keys [k_lo, k_hi) of sequence
-// b, slot -1 when it is the whole sequence (it writes the output), else the
-// partial slot of a piece of a sequence that spans bins.  first[i] ..
-// first[i+1] - 1 are bin i's segments.  The tables travel in kernel arguments
-// (2.9 KB and 0.8 KB).
-constexpr int AD_MAX_BINS = 64;
-constexpr int AD_MAX_SEGS = 160;
-struct DecodeSeg {
-    int b, k_lo, k_hi, slot;
-};
-struct DecodeBinTable {
-    int n_bins;
-    int first[AD_MAX_BINS + 1];
-    DecodeSeg seg[AD_MAX_SEGS];
-};
-// A split sequence b: its pieces' states sit in slots slot0 .. slot0 + n - 1.
-struct DecodeMerge {
-    int b, slot0, n;
-};
-struct DecodeMergeTable {
-    int n;
-    DecodeMerge e[AD_MAX_BINS];
-};
-
 struct DecodePlan {
     int n_chunks;
     int chunk;  // keys per chunk, multiple of 16
@@ -328,56 +302,6 @@ attn_decode_fused_kernel(AttnArgs a) {
     });
 }
 
-// Ragged batches: one workgroup per (bin, KV head) walks the bin's segments in
-// order.  A whole sequence writes its output; a piece writes its merged state to
-// its partial slot, and attn_decode_part_merge_kernel combines the pieces of a
-// sequence in order.  Every bin streams about the same number of keys, so the
-// longest sequence no longer sets the time.
-template <int HD, int G>
-__global__ void __launch_bounds__(64 * AD_FW)
-attn_decode_bins_kernel(AttnArgs a, DecodeBinTable t, float* __restrict__ part_o, float* __restrict__ part_ml) {
-    const int g = blockIdx.x % a.n_kv;
-    const int bin = blockIdx.x / a.n_kv;
-    for (int i = t.first[bin]; i < t.first[bin + 1]; ++i) {
-        const DecodeSeg sg = t.seg[i];
-        attend_unit<HD, G>(a, sg.b, g, sg.k_lo, sg.k_hi, [&](int h, int j, float mmax, float den, float num) {
-            const size_t hh = (size_t)g * G + h;
-            if (sg.slot < 0) {
-                ((bf16_t*)a.o)[((size_t)sg.b * a.n_heads + hh) * HD + j] = f2bf(num / den);
-            } else {
-                const size_t r = (size_t)sg.slot * a.n_heads + hh;
-                part_o[r * HD + j] = num;
-                if (j == 0) {
-                    part_ml[2 * r] = mmax;
-                    part_ml[2 * r + 1] = den;
-                }
-            }
-        });
-        __syncthreads();   // the next segment reuses the LDS of this one's merge
-    }
-}
-
-// One workgroup per (split sequence, query head): the pieces' states in slot
-// order, rescaled to a common maximum (the same rule as the chunk merge below).
-template <int HD>
-__global__ void __launch_bounds__(HD)
-attn_decode_part_merge_kernel(AttnArgs a, DecodeMergeTable t, const float* __restrict__ part_o,
-                              const float* __restrict__ part_ml) {
-    const DecodeMerge e = t.e[blockIdx.x / a.n_heads];
-    const size_t hh = blockIdx.x % a.n_heads;
-    const int j = threadIdx.x;
-    float mmax = -INFINITY;
-    for (int k = 0; k < e.n; ++k) mmax = fmaxf(mmax, part_ml[2 * ((size_t)(e.slot0 + k) * a.n_heads + hh)]);
-    float den = 0.f, num = 0.f;
-    for (int k = 0; k < e.n; ++k) {
-        const size_t r = (size_t)(e.slot0 + k) * a.n_heads + hh;
-        const float w = exp2f(part_ml[2 * r] - mmax);
-        den += w * part_ml[2 * r + 1];
-        num += w * part_o[r * HD + j];
-    }
-    ((bf16_t*)a.o)[((size_t)e.b * a.n_heads + hh) * HD + j] = f2bf(num / den);
-}
-
 // One workgroup per (sequence, query head): merge the chunk partials in order.
 template <int HD>
 __global__ void __launch_bounds__(HD)
@@ -414,63 +338,6 @@ hipError_t launch_fused(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int G>
-hipError_t launch_bins(const AttnArgs& a, const DecodeBinTable& t, float* part_o, float* part_ml, hipStream_t s) {
-    hipLaunchKernelGGL((attn_decode_bins_kernel<128, G>), dim3(t.n_bins * a.n_kv), dim3(64 * AD_FW), 0, s, a, t,
-                       part_o, part_ml);
-    return hipGetLastError();
-}
-
-// Packs the sequences of a ragged batch, in order, into n_bins bins of
-// capacity C = ceil(total keys / n_bins) rounded up to 16: a sequence that does
-// not fit the rest of the current bin continues in the next one (a bin closes
-// early rather than take a piece under 64 keys), and the last bin takes
-// whatever remains.  Used when the longest sequence exceeds 1.25 x the mean
-// (below that one workgroup per sequence is as even) and the tables fit.
-bool plan_ragged_bins(const int* pos, int B, int n_bins, DecodeBinTable& t, DecodeMergeTable& mt) {
-    long total = 0;
-    int lmax = 0;
-    for (int b = 0; b < B; ++b) {
-        total += (long)pos[b] + 1;
-        lmax = std::max(lmax, pos[b] + 1);
-    }
-    if (4L * lmax * B <= 5L * total) return false;
-    n_bins = std::max(1, std::min(n_bins, AD_MAX_BINS));
-    const long cap = std::max(16L, ((total + n_bins - 1) / n_bins + 15) / 16 * 16);
-    t.n_bins = n_bins;
-    mt.n = 0;
-    int bin = 0, nseg = 0, slots = 0;
-    long fill = 0;
-    t.first[0] = 0;
-    for (int b = 0; b < B; ++b) {
-        const int L = pos[b] + 1;
-        const int seg0 = nseg;
-        int lo = 0;
-        while (lo < L) {
-            long room = bin == n_bins - 1 ? (long)L : cap - fill;
-            if (room < std::min<long>(64, L - lo)) {   // close this bin, continue in the next
-                ++bin;
-                t.first[bin] = nseg;
-                fill = 0;
-                continue;
-            }
-            const int take = (int)std::min<long>(L - lo, room);
-            if (nseg == AD_MAX_SEGS) return false;
-            t.seg[nseg++] = DecodeSeg{b, lo, lo + take, -1};
-            fill += take;
-            lo += take;
-        }
-        const int pieces = nseg - seg0;
-        if (pieces > 1) {
-            if (mt.n == AD_MAX_BINS) return false;
-            mt.e[mt.n++] = DecodeMerge{b, slots, pieces};
-            for (int i = seg0; i < nseg; ++i) t.seg[i].slot = slots++;
-        }
-    }
-    for (int i = bin + 1; i <= n_bins; ++i) t.first[i] = nseg;
-    return true;
-}
-
 }  // namespace
 
 // Partials of the split form for any call reading at most n_keys keys: the
@@ -482,38 +349,6 @@ size_t attn_decode_ws_bytes(int B, int n_heads, int n_kv, int hd, int n_keys) {
     const int n_target = (AD_TARGET_WAVES + units - 1) / units;
     const int chunks = std::max(1, std::min(n_target, (n_keys + 15) / 16));
     return (size_t)B * n_heads * chunks * (hd + 2) * sizeof(float);
-}
-
-size_t attn_decode_parts_ws_bytes(int n_heads, int hd) {
-    return (size_t)AD_MAX_SEGS * n_heads * (hd + 2) * sizeof(float);
-}
-
-hipError_t attn_decode_ragged_launch(const AttnArgs& a, const int* pos_host, int num_cus, float* ws,
-                                     hipStream_t s, bool* launched) {
-    *launched = false;
-    if (a.hd != 128 || a.n_kv <= 0 || a.n_heads % a.n_kv != 0 || a.B <= 0 || !pos_host || num_cus <= 0)
-        return hipErrorInvalidValue;
-    if (a.B * a.n_kv < AD_FUSED_MIN_UNITS) return hipSuccess;   // the split form balances by chunks already
-    const int G = a.n_heads / a.n_kv;
-    if (G != 1 && G != 2 && G != 4 && G != 8) return hipSuccess;
-    DecodeBinTable t;
-    DecodeMergeTable mt;
-    if (!plan_ragged_bins(pos_host, a.B, num_cus / a.n_kv, t, mt)) return hipSuccess;
-    float* part_o = ws;
-    float* part_ml = ws + (size_t)AD_MAX_SEGS * a.n_heads * a.hd;
-    hipError_t err;
-    switch (G) {
-        case 1: err = launch_bins<1>(a, t, part_o, part_ml, s); break;
-        case 2: err = launch_bins<2>(a, t, part_o, part_ml, s); break;
-        case 4: err = launch_bins<4>(a, t, part_o, part_ml, s); break;
-        default: err = launch_bins<8>(a, t, part_o, part_ml, s); break;
-    }
-    if (err != hipSuccess) return err;
-    *launched = true;
-    if (mt.n == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_decode_part_merge_kernel<128>), dim3(mt.n * a.n_heads), dim3(128), 0, s, a, mt,
-                       part_o, part_ml);
-    return hipGetLastError();
 }
 
 hipError_t attn_decode_bf16_launch(const AttnArgs& a, float* ws, hipStream_t s) {

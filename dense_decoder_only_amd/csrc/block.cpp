@@ -287,9 +287,6 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
         }
         const size_t att = llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys);
         if (att > part) part = att;
-        // the pieces of a ragged batch's long sequences
-        const size_t rag = llb::attn_decode_parts_ws_bytes(c.n_heads, c.head_dim);
-        if (rag > part) part = rag;
     }
     if (decode) {  // per-sequence start positions of a ragged decode call
         p.pos = off;
@@ -419,19 +416,6 @@ llb_status run_proj(const llb_block* b, const llb::GemmArgs& a, bool small_m, fl
     return LLB_OK;
 }
 
-// bf16 decode attention: a ragged batch (pos_host: the host's start positions)
-// whose lengths are uneven enough runs as balanced parts; everything else one
-// workgroup per (sequence, KV head), or split over workgroups for few units.
-hipError_t attention_decode(const llb_block* b, const llb::AttnArgs& at, const int32_t* pos_host, float* part,
-                            hipStream_t s) {
-    if (pos_host) {
-        bool launched = false;
-        const hipError_t e = llb::attn_decode_ragged_launch(at, pos_host, b->num_cus, part, s, &launched);
-        if (e != hipSuccess || launched) return e;
-    }
-    return llb::attn_decode_bf16_launch(at, part, s);
-}
-
 // Blocks run back to back (a model) hand the attention RMSNorm of the next
 // block to the down projection of this one: its epilogue writes, besides
 // y = h + down, the next block's operand bf16(y * g1') and partial sums of y^2
@@ -552,7 +536,7 @@ llb_status run_block(llb_block* b, const float* x, float* y, int B, int T, int p
     at.pos_b = pos_b;
     hipError_t he;
     if (!bf16) he = llb::attn_f32_launch(at, s);
-    else if (decode) he = attention_decode(b, at, pos_host, part, s);
+    else if (decode) he = llb::attn_decode_bf16_launch(at, part, s);
     else he = llb::attn_prefill_bf16_launch(at, s);
     if (he != hipSuccess) return hip_fail(he, "attention");
     if ((te = mark()) != hipSuccess) return hip_fail(te, "stage timing");
@@ -936,11 +920,10 @@ llb_status llb_attention_prefill(const llb_block* b, const void* q, const void* 
 size_t llb_attention_workspace_bytes(const llb_block* b, int32_t B, int32_t n_keys) {
     if (!handle_ok(b) || B <= 0 || n_keys <= 0) return 0;
     const llb_config& c = b->cfg;
-    // partials (split form, or the pieces of a ragged batch), then B start positions
+    // partials of the split form, then B start positions
     const size_t pos = align_up((size_t)B * sizeof(int32_t));
     if (c.wdtype == LLB_F32) return 256 + pos;
-    return align_up(std::max(llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys),
-                             llb::attn_decode_parts_ws_bytes(c.n_heads, c.head_dim))) + pos;
+    return align_up(llb::attn_decode_ws_bytes(B, c.n_heads, c.n_kv_heads, c.head_dim, n_keys)) + pos;
 }
 
 llb_status llb_attention_decode(const llb_block* b, const void* q, const void* k_cache,
@@ -1014,7 +997,7 @@ llb_status llb_attention_decode_ragged(const llb_block* b, const void* q, const 
     hipError_t e = llb::store_ints_launch(pos_dev, start_pos, B, s);
     if (e != hipSuccess) return hip_fail(e, "start positions");
     at.pos_b = pos_dev;
-    e = c.wdtype == LLB_F32 ? llb::attn_f32_launch(at, s) : attention_decode(b, at, start_pos, (float*)ws, s);
+    e = c.wdtype == LLB_F32 ? llb::attn_f32_launch(at, s) : llb::attn_decode_bf16_launch(at, (float*)ws, s);
     if (e != hipSuccess) return hip_fail(e, "attention decode");
     return LLB_OK;
 }

@@ -133,16 +133,6 @@ hipError_t attn_prefill_bf16_launch(const AttnArgs& a, hipStream_t s);
 // Split-K decode attention + merge.  ws: attn_decode_ws_bytes(...) bytes.
 size_t attn_decode_ws_bytes(int B, int n_heads, int n_kv, int hd, int n_keys);
 hipError_t attn_decode_bf16_launch(const AttnArgs& a, float* ws, hipStream_t s);
-// Decode attention of a ragged batch (sequence b reads keys 0..pos_host[b];
-// pos_host on the host): when the batch has enough (sequence, KV head) units for
-// one workgroup per unit and its longest sequence is well above the mean, the
-// keys are packed into num_cus / n_kv bins of equal size, one workgroup per
-// (bin, KV head); sequences that span bins are merged in order by a second
-// kernel.  *launched tells whether it ran (false: use attn_decode_bf16_launch
-// with a.pos_b).  ws: attn_decode_parts_ws_bytes.
-size_t attn_decode_parts_ws_bytes(int n_heads, int hd);
-hipError_t attn_decode_ragged_launch(const AttnArgs& a, const int* pos_host, int num_cus, float* ws,
-                                     hipStream_t s, bool* launched);
 // Plain fp32 attention (prefill or decode, any T).
 hipError_t attn_f32_launch(const AttnArgs& a, hipStream_t s);
 

@@ -230,10 +230,8 @@ size_t llb_attention_workspace_bytes(const llb_block* blk, int32_t B, int32_t n_
  * own position start_pos[b] (a HOST array of B entries, read during the call)
  * and reads keys 0..start_pos[b] of its sequence (L_b = start_pos[b] + 1 keys,
  * "Llama 3 8B - Prepare Q, K, V", header; per-sequence lengths are this
- * library's extension).  The same attention llb_block_decode_ragged runs: when
- * the lengths are uneven, long sequences are cut into pieces of about the mean
- * length whose states are merged in order.  ws: llb_attention_workspace_bytes(blk,
- * B, max_b start_pos[b] + 1) bytes. */
+ * library's extension).  The same attention llb_block_decode_ragged runs.
+ * ws: llb_attention_workspace_bytes(blk, B, max_b start_pos[b] + 1) bytes. */
 llb_status llb_attention_decode_ragged(const llb_block* blk, const void* q, const void* k_cache,
                                        const void* v_cache, void* o, int32_t B, const int32_t* start_pos,
                                        int32_t cache_cap, void* ws, size_t ws_bytes, void* stream);
