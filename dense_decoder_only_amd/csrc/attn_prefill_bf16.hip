@@ -411,7 +411,7 @@ hipError_t attn_prefill_bf16_launch(const AttnArgs& a, hipStream_t s) {
         case 1: return launch_g<1, 2, 2>(a, s);
         case 2: return launch_g<2, 2, 2>(a, s);
         case 4: return launch_g<4, 2, 2>(a, s);
-        case 8: return launch_g<8, 1, 3>(a, s);
+        case 8: return launch_g<8, 1, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
