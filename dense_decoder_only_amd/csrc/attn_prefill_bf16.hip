@@ -47,6 +47,8 @@ constexpr int AP_BQ = 32;        // query positions per block
 constexpr int AP_BKV = 64;       // keys per wave tile
 constexpr int AP_TILE_BYTES = AP_BKV * AP_HD * 2;   // one K (or V) tile: 16 KB
 constexpr float LAZY_LOG2 = 8.0f;
+constexpr int AP_KD = 2;         // K fragments are read this many k-steps ahead of their MFMAs
+constexpr int AP_VD = 1;         // V^T fragments this many 16-key steps ahead
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -215,30 +217,34 @@ attn_prefill_kernel(AttnArgs a) {
         for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[ms][r] = 0.f;
-        // K fragments are read two k-steps ahead of the MFMAs that use them
-        uint4 kf[3][2];
+        // K fragments are read AP_KD k-steps ahead of the MFMAs that use them
+        constexpr int KR = AP_KD + 1;
+        uint4 kf[KR][2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < AP_KD; ++kk) {
             kf[kk][0] = lds_read_b128(kb + kaddr[kk]);
             kf[kk][1] = lds_read_b128(kb + 32 * 256 + kaddr[kk]);
         }
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            if (kk + 2 < 8) {
-                kf[(kk + 2) % 3][0] = lds_read_b128(kb + kaddr[kk + 2]);
-                kf[(kk + 2) % 3][1] = lds_read_b128(kb + 32 * 256 + kaddr[kk + 2]);
+            if (kk + AP_KD < 8) {
+                kf[(kk + AP_KD) % KR][0] = lds_read_b128(kb + kaddr[kk + AP_KD]);
+                kf[(kk + AP_KD) % KR][1] = lds_read_b128(kb + 32 * 256 + kaddr[kk + AP_KD]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            s[0] = mfma32(as_bf16x8(kf[kk % 3][0]), qf[kk], s[0]);
-            s[1] = mfma32(as_bf16x8(kf[kk % 3][1]), qf[kk], s[1]);
+            s[0] = mfma32(as_bf16x8(kf[kk % KR][0]), qf[kk], s[0]);
+            s[1] = mfma32(as_bf16x8(kf[kk % KR][1]), qf[kk], s[1]);
         }
-        // V^T fragments of the first 16 keys, read while the softmax runs
-        uint2 vf[2][4][2];
+        // V^T fragments of the first AP_VD 16-key steps, read while the softmax runs
+        constexpr int VR = AP_VD + 1;
+        uint2 vf[VR][4][2];
 #pragma unroll
-        for (int os = 0; os < 4; ++os) {
-            vf[0][os][0] = lds_read_tr16(vb + vaddr[os]);
-            vf[0][os][1] = lds_read_tr16(vb + 8 * 256 + vaddr[os]);
-        }
+        for (int ks = 0; ks < AP_VD; ++ks)
+#pragma unroll
+            for (int os = 0; os < 4; ++os) {
+                vf[ks][os][0] = lds_read_tr16(vb + ks * 16 * 256 + vaddr[os]);
+                vf[ks][os][1] = lds_read_tr16(vb + ks * 16 * 256 + 8 * 256 + vaddr[os]);
+            }
         if (key0 + AP_BKV - 1 > q_first) {  // tile reaches the diagonal
             const int lim = my_pos - key0 - 4 * hf;  // mask key offsets > lim
 #pragma unroll
@@ -284,17 +290,18 @@ attn_prefill_kernel(AttnArgs a) {
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(pw[e], ones, l_run, false);
             }
             const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-            if (ks + 1 < 4) {
+            if (ks + AP_VD < 4) {
 #pragma unroll
                 for (int os = 0; os < 4; ++os) {
-                    vf[(ks + 1) & 1][os][0] = lds_read_tr16(vb + (ks + 1) * 16 * 256 + vaddr[os]);
-                    vf[(ks + 1) & 1][os][1] = lds_read_tr16(vb + (ks + 1) * 16 * 256 + 8 * 256 + vaddr[os]);
+                    vf[(ks + AP_VD) % VR][os][0] = lds_read_tr16(vb + (ks + AP_VD) * 16 * 256 + vaddr[os]);
+                    vf[(ks + AP_VD) % VR][os][1] =
+                        lds_read_tr16(vb + (ks + AP_VD) * 16 * 256 + 8 * 256 + vaddr[os]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int os = 0; os < 4; ++os) {
-                const uint2 lo = vf[ks & 1][os][0], hi = vf[ks & 1][os][1];
+                const uint2 lo = vf[ks % VR][os][0], hi = vf[ks % VR][os][1];
                 oacc[os] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf, oacc[os]);
             }
         }
