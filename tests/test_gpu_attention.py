@@ -79,15 +79,16 @@ def test_attention_prefill_random(G, B, T, pos0):
         llb.llb_block_destroy(blk)
 
 
+@pytest.mark.parametrize("G", [4, 8])
 @pytest.mark.parametrize("shift,pos0,T", [(0, 0, 127), (1, 0, 127), (0, 200, 100), (1, 200, 100),
                                            (1, 0, 64), (1, 31, 33)])
-def test_attention_prefill_structured_mask(shift, pos0, T):
+def test_attention_prefill_structured_mask(shift, pos0, T, G):
     """Key n is 4 * e_(n mod 128); the query at position p is c * e_((p + shift) mod 128)
     with a score of 30 for a matching key and 0 otherwise.  shift=0: the query's
     own key dominates (dropping the diagonal from the mask would show); shift=1:
     the next, future key would dominate if the mask leaked it.  Softmax weights
     are exactly 1 or ~e^-30, so only the bf16 output rounding remains."""
-    shp, blk, _ = _block(4)
+    shp, blk, _ = _block(G)
     try:
         B, H, Hkv, hd = 1, shp.n_heads, 2, 128
         cap = workloads.cache_capacity(pos0 + T)
@@ -99,7 +100,7 @@ def test_attention_prefill_structured_mask(shift, pos0, T):
         q = torch.zeros(B, H, T, hd, dtype=torch.bfloat16)
         for t in range(T):
             q[:, :, t, (pos0 + t + shift) % 128] = 30.0 * math.sqrt(hd) / 4.0
-        note(f"attn prefill structured shift={shift} pos0={pos0} T={T}")
+        note(f"attn prefill structured G={G} shift={shift} pos0={pos0} T={T}")
         o = torch.empty(B, T, H * hd, dtype=torch.bfloat16, device="cuda")
         llb.llb_attention_prefill(blk, q.cuda(), kc.cuda(), vc.cuda(), o, B, T, pos0, cap)
         ref = _oracle_prefill(q, kc, vc, pos0, T)
@@ -110,12 +111,13 @@ def test_attention_prefill_structured_mask(shift, pos0, T):
         llb.llb_block_destroy(blk)
 
 
-def test_attention_prefill_growing_scores():
+@pytest.mark.parametrize("G", [4, 8])
+def test_attention_prefill_growing_scores(G):
     """Scores rise along the keys (score of key n for the query at p is
     0.05 n + noise), so the softmax offset keeps moving up tile after tile:
     a running maximum that is not raised far enough, or a rescale that is
     applied to the wrong rows, shows as a relative error far above bf16."""
-    shp, blk, _ = _block(4)
+    shp, blk, _ = _block(G)
     try:
         B, H, Hkv, hd = 1, shp.n_heads, 2, 128
         T, pos0 = 900, 0
