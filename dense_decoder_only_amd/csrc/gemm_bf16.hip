@@ -92,19 +92,48 @@ gemm_bf16_kernel(GemmArgs args) {
     const int tiles_m = (M + BM - 1) / BM;
     const int n_begin = args.n_begin;
     const int tiles_n = ((args.n_end ? args.n_end : N) - n_begin) / BN;
-    // Tile order: consecutive ids run on one XCD (xcd_remap); within the id
-    // sequence, groups of up to 8 row panels are walked column by column, so the
-    // ~32 tiles an XCD runs at once form an 8 x 4 block that shares A and W
-    // panels in that XCD's L2.
-    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs, and
+    // each XCD runs about 32 tiles at a time.  The 32 tiles of an XCD form an
+    // 8 x 4 block of the tile grid (8 row panels x 4 column panels: the fewest
+    // operand panels that 32 tiles can share in the XCD's L2).  The 256 tiles
+    // of the chip form one (8 XR) x (4 XC) block (XR x XC = 8 XCDs, as square
+    // as the grid allows), so that the operand panels the XCDs refill from
+    // beyond their L2 are largely the same panels, served by the shared last
+    // level cache rather than by HBM; the blocks walk the columns of a band of
+    // 8 XR row panels.  Grids that no such block divides fall back to XCDs
+    // owning the columns n = x (mod 8) and walking groups of 8 row panels
+    // together, or to consecutive ids per XCD (xcd_remap).
     constexpr int GM = 8;
-    const int group = tile / (GM * tiles_n);
-    const int first_m = group * GM;
-    const int gm = min(tiles_m - first_m, GM);
-    const int in_group = tile - group * (GM * tiles_n);
-    const int m0 = (first_m + in_group % gm) * BM;
-    const int tn = in_group / gm;
-    const int n0 = n_begin + tn * BN;
+    const int xr = (tiles_m % 16 == 0 && tiles_n % 16 == 0) ? 2
+                   : (tiles_m % 32 == 0 && tiles_n % 8 == 0) ? 4
+                   : (tiles_m % 8 == 0 && tiles_n % 32 == 0) ? 1 : 0;
+    int m0, n0;
+    if (xr) {
+        const int xc = 8 / xr;
+        const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+        const int r = j / 32, w = j % 32;          // chip block, place in the XCD's 8 x 4
+        const int ncb = tiles_n / (4 * xc);
+        const int rb = r / ncb, cb = r % ncb;
+        m0 = (rb * 8 * xr + (x % xr) * 8 + w % 8) * BM;
+        n0 = n_begin + (cb * 4 * xc + (x / xr) * 4 + w / 8) * BN;
+    } else if (tiles_n % 8 == 0) {
+        const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+        const int ncx = tiles_n / 8;
+        const int group = j / (GM * ncx);
+        const int first_m = group * GM;
+        const int gm = min(tiles_m - first_m, GM);
+        const int in_group = j - group * (GM * ncx);
+        m0 = (first_m + in_group % gm) * BM;
+        n0 = n_begin + ((in_group / gm) * 8 + x) * BN;
+    } else {
+        const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+        const int group = tile / (GM * tiles_n);
+        const int first_m = group * GM;
+        const int gm = min(tiles_m - first_m, GM);
+        const int in_group = tile - group * (GM * tiles_n);
+        m0 = (first_m + in_group % gm) * BM;
+        n0 = n_begin + (in_group / gm) * BN;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
