@@ -162,6 +162,24 @@ def test_bf16_prefill_every_tile_config(cfg):
     assert ran, "no projection accepted the configuration"
 
 
+# Grids whose column-panel count is a multiple of 8 while the row-panel count is
+# not a multiple of 8 (nor 16 or 32) take the prefill GEMM's column-interleaved
+# tile order (XCD x on the column panels n = x mod 8, groups of 8 row panels, the
+# last group short): d = d_ff = 2048 gives 8 or 16 column panels for the O, down
+# and gate/up projections, T = 300 and 2100 give 2 and 9 row panels.  (The 70B
+# and 8B full-size tests take the 16 x 16, 32 x 8 and 8 x 32 block orders.)
+@pytest.mark.parametrize("T", [300, 2100])
+def test_bf16_prefill_column_interleaved_tile_order(T):
+    shp = shape(d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128, d_ff=2048, rope_scaling=False)
+    y, kd, vd, y_ref, k_ref, v_ref = _run_prefill(shp, 321 + T, 1, T)
+    e_y = rel_err(y, y_ref)
+    e_k = bf16_err(kd[:, :, :T], k_ref)
+    e_v = bf16_err(vd[:, :, :T], v_ref)
+    note(f"  y {e_y:.2e}  k {e_k:.3f}  v {e_v:.3f}")
+    assert e_y <= 2e-2 and e_k <= 1.0 and e_v <= 1.0
+    assert torch.all(kd[:, :, T:].float() == SENTINEL)
+
+
 def test_tile_override_rejects_bad_values():
     from dense_decoder_only_amd import llb
     shp = shape(**TILE_SHAPE, rope_scaling=False)
