@@ -310,8 +310,11 @@ gemm_bf16_kernel(GemmArgs args) {
             else if (n <= TNB) fb[fbuf][n - 1] = *(lds_frag_ptr)(uintptr_t)(bb + (n - 1) * MB * BK * 2);
             else fa[fbuf][n - TNB] = *(lds_frag_ptr)(uintptr_t)(ab + (n - TNB) * MB * BK * 2);
         };
-        auto mf = [&](int fbuf, int n) {  // n-th of the NM MFMAs of a k-step
-            const int i = n / TNB, j = n % TNB;
+        // n-th of the NM MFMAs of a k-step, in serpentine order (odd block rows
+        // walk j downwards, so consecutive MFMAs always share an operand:
+        // measured 0.4% faster on the 70B gate/up than plain row order)
+        auto mf = [&](int fbuf, int n) {
+            const int i = n / TNB, j = (i & 1) ? TNB - 1 - n % TNB : n % TNB;
             if constexpr (M16) acc16[i][j] = mfma16(fa[fbuf][i], fb[fbuf][j], acc16[i][j]);
             else acc[i][j] = mfma32(fa[fbuf][i], fb[fbuf][j], acc[i][j]);
         };
