@@ -1,5 +1,5 @@
 // Measurement probes: the streaming rate of HBM and the bf16 MFMA rate that the
-// chip sustains on the box in use, the denominators of the measured roofline
+// chip sustains on the card in use, the denominators of the measured roofline
 // fractions next to the nominal ones (8 TB/s, 2.5 PFLOP/s dense bf16).
 //
 //  - probe_read_kernel: every workgroup streams a contiguous share of a buffer
