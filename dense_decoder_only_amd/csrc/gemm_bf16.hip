@@ -327,7 +327,13 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
         for (int i = 0; i < L; ++i)
             voff[i] = (uint32_t)((const char*)src[i] - (const char*)(i < NA ? A : W));
-        auto dma_one = [&](int kt, int st, int i) {
+        // The c-th copy a k-tile issues moves block i: the W blocks go first.
+        // W is the operand that streams from HBM (the A panels of a band stay
+        // in the last-level cache), so its copies get the most time to land
+        // before the wait (measured 1.3% faster on the 70B prefill than A
+        // first, 0.7% on the 8B).
+        auto dma_one = [&](int kt, int st, int c) {
+            const int i = c < L - NA ? NA + c : c - (L - NA);
             const int blk = wave + i * NW;
             const char* sb = i < NA ? (const char*)A + (size_t)kt * BK * 2 : (const char*)W + k_off(NA, kt) * 2;
             dma16_s(voff[i], sb, lds_base + (uint32_t)((st * STAGE_ELEMS + blk * RPB * BK) * sizeof(bf16_t)));
@@ -352,8 +358,9 @@ gemm_bf16_kernel(GemmArgs args) {
         for (int t = nk; t < STAGES - 1; ++t)
             for (int i = 0; i < L; ++i) dma_one(nk - 1, t, i);
         // SPREAD: the first CA copies of k-tile STAGES-1, as the second half of
-        // a previous k-tile would have issued them
-        constexpr int CA = SPREAD ? L / 4 : 0;
+        // a previous k-tile would have issued them (an eighth of the copies:
+        // with W first, a quarter or more was slower, none no faster)
+        constexpr int CA = SPREAD ? L / 8 : 0;
         static_assert(!SPREAD || KS >= 2, "spread copies: two or more k-steps");
         if constexpr (SPREAD)
             for (int i = 0; i < CA; ++i) dma_one(min(STAGES - 1, nk - 1), STAGES - 1, i);
