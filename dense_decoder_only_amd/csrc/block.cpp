@@ -307,12 +307,17 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 //    operand (70B: 1.87 against 2.03 ms on the 8-wave kernel) and long K (the
 //    down projection) the interleaved kernel on 16x16x32 MFMAs with the L2
 //    prefetch and spread copies, for the others the interleaved 32x32x16
-//    kernel with the prefetch at large N and the 8-wave kernel otherwise;
+//    kernel with the prefetch at large N and the 8-wave kernel otherwise; the
+//    gate/up projection, whose band of A panels stays in the last-level cache
+//    over 14 column blocks, prefetches W lines only (70B gate/up -2%; the
+//    down projection, whose A streams from HBM, is 5% slower that way);
 //  - 256x192 tiles when they fill whole rounds of the 256 compute units (the
-//    QKV projection on the 16x16x32 prefetching spread-copy kernel, others on
-//    the interleaved 32x32x16 kernel);
+//    QKV projection on the 16x16x32 spread-copy kernel prefetching W lines
+//    only, the whole A being cache-resident at these sizes (8B QKV -4%);
+//    others on the interleaved 32x32x16 kernel);
 //  - 256x256 tiles once they fill at least 160 compute units (gate/up on the
-//    16x16x32 prefetching spread-copy kernel, the rest on the 8-wave kernel);
+//    16x16x32 spread-copy kernel prefetching W lines only, 8B gate/up -3%;
+//    the rest on the 8-wave kernel);
 //  - 256x128 tiles (interleaved, BK 64, 3 stages; spread copies for the
 //    residual-only epilogue, the down projection) from 192 tiles up when K is
 //    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that;
@@ -324,10 +329,11 @@ int pick_tile(int M, int N, int K, int epi) {
     if (!llb::gemm_bf16_offsets_fit(M, N, K))  // beyond the interleaved schedules' reach
         return N % 256 == 0 ? 0 : N % 128 != 0 ? -1 : M > 128 ? 1 : 2;
     if (N % 256 == 0 && M >= 4096)
-        return (scaled || K >= 16384 || epi == llb::EPI_RESID_NORM) ? 14 : N >= 32768 ? 4 : 0;
+        return epi == llb::EPI_SWIGLU ? 17
+               : (scaled || K >= 16384 || epi == llb::EPI_RESID_NORM) ? 14 : N >= 32768 ? 4 : 0;
     if (N % 128 != 0) return -1;
-    if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 15 : 6;
-    if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 14 : 0;
+    if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 18 : 6;
+    if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 17 : 0;
     const long t128 = (long)pm * (N / 128);
     if (t128 >= 192 && K % 64 == 0) return epi == llb::EPI_RESID ? 16 : 7;
     return M > 128 ? 1 : 2;

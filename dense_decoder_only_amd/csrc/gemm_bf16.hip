@@ -48,9 +48,11 @@ LLB_DEV int swz(int r) {
 // prefetch of the operand lines two k-tiles ahead of the copies), all on
 // 32x32x16 MFMAs; SCHED_I16 and SCHED_I16_PF are the interleaved schedules on
 // 16x16x32 MFMAs, which do the same work at a lower power draw (more clock
-// under the chip's power limit, measured on random operands).
+// under the chip's power limit, measured on random operands).  Flags:
+// SCHED_SPREAD (below) and SCHED_PF_W_ONLY, which prefetches the W lines only,
+// for projections whose A panels the last-level cache already holds.
 constexpr int SCHED_PLAIN = 0, SCHED_INTERLEAVE = 1, SCHED_INTERLEAVE_PF = 2, SCHED_I16 = 3,
-              SCHED_I16_PF = 4, SCHED_SPREAD = 8;
+              SCHED_I16_PF = 4, SCHED_SPREAD = 8, SCHED_PF_W_ONLY = 16;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES, int OCC, int EPI, int SCHED>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(OCC)))
@@ -344,13 +346,18 @@ gemm_bf16_kernel(GemmArgs args) {
         // slot.  The copies of k-tile t+1 then mostly hit in L2.  The two
         // prefetch loads are issued after the tile's copies, so waiting for the
         // copies leaves them in flight (vector memory loads complete in order).
-        constexpr int NPF = PF_DIST > 0 ? 2 : 0;
+        // SCHED_PF_W_ONLY drops the A line: where a band's A panels stay in the
+        // last-level cache (the gate/up projection walks 7 to 14 column blocks
+        // per band; an 8B prefill's whole A is 16 MB) its prefetch only adds
+        // traffic and a load for the waits to cover.
+        constexpr bool PF_A = (SCHED & SCHED_PF_W_ONLY) == 0;
+        constexpr int NPF = PF_DIST > 0 ? (PF_A ? 2 : 1) : 0;
         const bf16_t* pf_a = A + (size_t)min(m0 + (wave * 64 + lane) % BM, M - 1) * K;
         const int pf_n = n0 + (wave * 64 + lane) % BN;
         const bf16_t* pf_w = W + (size_t)(pf_n >> 7) * (K / 64) * 8192 + (pf_n & 127) * 64;
         const uint32_t pf_lds = lds_base + (uint32_t)(STAGES * STAGE_ELEMS * 2) + wave * 256;
         auto prefetch = [&](int kt) {
-            dma4(pf_a + (size_t)kt * BK, pf_lds);
+            if constexpr (PF_A) dma4(pf_a + (size_t)kt * BK, pf_lds);
             dma4(pf_w + (size_t)(BK == 64 ? kt : kt >> 1) * 8192, pf_lds);
         };
         // the prologue issued k-tiles 0..STAGES-2 (clamped copies for small K
@@ -601,8 +608,9 @@ tile_weights_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, in
 struct TileCfg {
     int bm, bn, wm, wn, bk, stages, occ, sched;
 };
-// The first three are the configurations the host chooses between; the rest
-// are kept for tuning experiments.
+// The host picks one per projection from its shape and epilogue (0, 1, 2, 4,
+// 6, 7, 14, 16, 17, 18 on the shapes measured); the others stay for tuning and
+// are covered by the parity tests like the rest.
 constexpr TileCfg kTiles[] = {
     {256, 256, 4, 2, 64, 2, 2, 0},  // 8 waves (2 per SIMD), wave tile 64x128, BK 64, 128 KB LDS
     {256, 128, 2, 2, 32, 3, 2, 0},  // 4 waves, wave tile 128x64, 72 KB: 2 workgroups per CU
@@ -621,6 +629,8 @@ constexpr TileCfg kTiles[] = {
     {256, 256, 2, 2, 64, 2, 1, 4 + 8},  // 10 with spread copies
     {256, 192, 2, 2, 64, 2, 1, 4 + 8},  // 13 with spread copies
     {256, 128, 2, 2, 64, 3, 1, 1 + 8},  // 7 with spread copies
+    {256, 256, 2, 2, 64, 2, 1, 4 + 8 + 16},  // 14 prefetching W lines only
+    {256, 192, 2, 2, 64, 2, 1, 4 + 8 + 16},  // 15 prefetching W lines only
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -711,7 +721,11 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int cfg, hipStream_t s) {
         case 13: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF>(a, s);
         case 14: return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD>(a, s);
         case 15: return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD>(a, s);
-        default: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_INTERLEAVE + SCHED_SPREAD>(a, s);
+        case 16: return launch_cfg<256, 128, 2, 2, 64, 3, 1, SCHED_INTERLEAVE + SCHED_SPREAD>(a, s);
+        case 17:
+            return launch_cfg<256, 256, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD + SCHED_PF_W_ONLY>(a, s);
+        default:
+            return launch_cfg<256, 192, 2, 2, 64, 2, 1, SCHED_I16_PF + SCHED_SPREAD + SCHED_PF_W_ONLY>(a, s);
     }
 }
 
