@@ -102,7 +102,9 @@ gemm_bf16_kernel(GemmArgs args) {
     // as the grid allows), so that the operand panels the XCDs refill from
     // beyond their L2 are largely the same panels, served by the shared last
     // level cache rather than by HBM; the blocks walk the columns of a band of
-    // 8 XR row panels.  Grids that no such block divides fall back to XCDs
+    // 8 XR row panels, every other band from the right, so that a band starts
+    // on the W panels the previous one ended on (measured 0.25% faster on the
+    // 70B prefill).  Grids that no such block divides fall back to XCDs
     // owning the columns n = x (mod 8) and walking groups of 8 row panels
     // together, or to consecutive ids per XCD (xcd_remap).
     constexpr int GM = 8;
@@ -115,7 +117,7 @@ gemm_bf16_kernel(GemmArgs args) {
         const int x = blockIdx.x % 8, j = blockIdx.x / 8;
         const int r = j / 32, w = j % 32;          // chip block, place in the XCD's 8 x 4
         const int ncb = tiles_n / (4 * xc);
-        const int rb = r / ncb, cb = r % ncb;
+        const int rb = r / ncb, cb = (rb & 1) ? ncb - 1 - r % ncb : r % ncb;
         m0 = (rb * 8 * xr + (x % xr) * 8 + w % 8) * BM;
         n0 = n_begin + (cb * 4 * xc + (x / xr) * 4 + w / 8) * BN;
     } else if (tiles_n % 8 == 0) {
