@@ -104,11 +104,17 @@ gemm_bf16_kernel(GemmArgs args) {
     // level cache rather than by HBM; the blocks walk the columns of a band of
     // 8 XR row panels, every other band from the right, so that a band starts
     // on the W panels the previous one ended on (measured 0.25% faster on the
-    // 70B prefill).  Grids that no such block divides fall back to XCDs
+    // 70B prefill).  The gate/up projection (SwiGLU epilogue) takes the taller
+    // 32 x 8 block where it divides the grid: its band of A panels (128 MB)
+    // stays in the last-level cache, and each round then fetches 8 W panels
+    // from HBM instead of 16 (measured 0.6% faster on the 70B prefill; the
+    // residual projections, whose A streams, are faster on 16 x 16).  Grids
+    // that no such block divides fall back to XCDs
     // owning the columns n = x (mod 8) and walking groups of 8 row panels
     // together, or to consecutive ids per XCD (xcd_remap).
     constexpr int GM = 8;
-    const int xr = (tiles_m % 16 == 0 && tiles_n % 16 == 0) ? 2
+    const int xr = (EPI == EPI_SWIGLU && tiles_m % 32 == 0 && tiles_n % 8 == 0) ? 4
+                   : (tiles_m % 16 == 0 && tiles_n % 16 == 0) ? 2
                    : (tiles_m % 32 == 0 && tiles_n % 8 == 0) ? 4
                    : (tiles_m % 8 == 0 && tiles_n % 32 == 0) ? 1 : 0;
     int m0, n0;
