@@ -482,6 +482,85 @@ gemm_bf16_kernel(GemmArgs args) {
         if (tid < BM) sScale[tid] = row_scale;
         __syncthreads();
     }
+    // Residual epilogues: a lane's 8 columns are the same in every slice, so
+    // its gains are loaded once, and the residual rows of the next slice are
+    // loaded before the current slice's stores.  Vector-memory operations
+    // complete in order, so a load issued after a store waits for that store
+    // too; issued this way, each slice waits for one load issued a slice
+    // earlier instead of one round trip per chunk (70B O projection 3% and
+    // 8B O 5% faster than loading each chunk's residual and gains in turn).
+    constexpr int RCPR = WTN / 8;                       // 8-column chunks per row
+    // (slices whose chunk count does not divide into lanes keep the plain flush)
+    constexpr bool RES = (EPI == EPI_RESID || EPI == EPI_RESID_NORM) && 64 % RCPR == 0 &&
+                         (HR * RCPR) % 64 == 0;
+    constexpr int RIT = RES ? HR * RCPR / 64 : 1;       // chunks per lane per slice
+    const int rch = lane % RCPR;
+    const int rn = n0 + wn * WTN + rch * 8;
+    float4 rcur[RIT][2], rnext[RIT][2];
+    float rg[8];
+    auto load_res = [&](int rbase, float4 (&r)[RIT][2]) {
+#pragma unroll
+        for (int k = 0; k < RIT; ++k) {
+            const int m = min(m0 + rbase + lane / RCPR + k * (64 / RCPR), M - 1);
+            const float* p = e.resid + (size_t)m * N + rn;
+            r[k][0] = *(const float4*)p;
+            r[k][1] = *(const float4*)(p + 4);
+        }
+    };
+    if constexpr (RES) {
+        if constexpr (EPI == EPI_RESID_NORM) {
+            *(float4*)&rg[0] = *(const float4*)(e.gain + rn);
+            *(float4*)&rg[4] = *(const float4*)(e.gain + rn + 4);
+        }
+        load_res(wm * WTM, rcur);
+    }
+    auto flush_res = [&](int rbase, int next_rbase) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (next_rbase >= 0) load_res(next_rbase, rnext);
+#pragma unroll
+        for (int k = 0; k < RIT; ++k) {
+            const int row = lane / RCPR + k * (64 / RCPR);
+            const int m = m0 + rbase + row;
+            const float4 s0 = *(const float4*)&stile[row * SROW + rch * 8];
+            const float4 s1 = *(const float4*)&stile[row * SROW + rch * 8 + 4];
+            float v[8];
+            v[0] = s0.x + rcur[k][0].x; v[1] = s0.y + rcur[k][0].y;
+            v[2] = s0.z + rcur[k][0].z; v[3] = s0.w + rcur[k][0].w;
+            v[4] = s1.x + rcur[k][1].x; v[5] = s1.y + rcur[k][1].y;
+            v[6] = s1.z + rcur[k][1].z; v[7] = s1.w + rcur[k][1].w;
+            float ss = 0.f;
+            if (m < M) {
+                const size_t idx = (size_t)m * N + rn;
+                *(float4*)(e.out + idx) = make_float4(v[0], v[1], v[2], v[3]);
+                *(float4*)(e.out + idx + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                if constexpr (EPI == EPI_RESID_NORM) {
+                    float t[8];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) t[c] = v[c] * rg[c];
+                    *(uint4*)((bf16_t*)e.a_out + idx) = pack8(t);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) ss += v[c] * v[c];
+                }
+            }
+            if constexpr (EPI == EPI_RESID_NORM) {
+#pragma unroll
+                for (int off = 1; off < RCPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                if (rch == 0) sPart[wn * BM + rbase + row] = ss;
+            }
+        }
+        if (next_rbase >= 0) {
+#pragma unroll
+            for (int k = 0; k < RIT; ++k) {
+                rcur[k][0] = rnext[k][0];
+                rcur[k][1] = rnext[k][1];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
     // the staged rows rbase .. rbase + HR - 1 of this wave's slice, from LDS to
     // the epilogue
     auto flush = [&](int rbase) {
@@ -555,7 +634,8 @@ gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
                 for (int j = 0; j < TNB; ++j) stile[rr * SROW + j * 16 + (lane & 15)] = acc16[i][j][r] * sc;
             }
-            flush(rbase);
+            if constexpr (RES) flush_res(rbase, i + 1 < TMB ? rbase + 16 : -1);
+            else flush(rbase);
         }
     } else {
 #pragma unroll
@@ -579,7 +659,8 @@ gemm_bf16_kernel(GemmArgs args) {
                     for (int j = 0; j < TN; ++j)
                         stile[rr * SROW + j * 32 + (lane & 31)] = acc[i][j][r] * sc;
                 }
-                flush(rbase);
+                if constexpr (RES) flush_res(rbase, half == 0 ? rbase + HR : i + 1 < TM ? rbase + HR : -1);
+                else flush(rbase);
             }
         }
     }
