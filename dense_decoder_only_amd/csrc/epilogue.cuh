@@ -68,6 +68,13 @@ LLB_DEV void epi_norm_operand(const Epilogue& e, int m, int n, int N, float h) {
     ((bf16_t*)e.a_out)[(size_t)m * N + n] = f2bf(h * e.gain[n]);
 }
 
+// The same with the gain g = gain[n] loaded ahead: vector-memory operations
+// complete in order, so a gain load issued after the residual store would wait
+// for that store as well.
+LLB_DEV void epi_norm_operand_g(const Epilogue& e, int m, int n, int N, float h, float g) {
+    ((bf16_t*)e.a_out)[(size_t)m * N + n] = f2bf(h * g);
+}
+
 // gate = C[m, 64*grp + j], up = C[m, 64*grp + 32 + j]; feature f = 32*grp + j.
 template <typename OT>
 LLB_DEV void epi_swiglu(const Epilogue& e, int m, int f, int d_ff, float gate, float up) {
@@ -133,6 +140,25 @@ LLB_DEV void epi_resid8(const Epilogue& e, int m, int n, int N, float* v) {
     v[4] += r1.x; v[5] += r1.y; v[6] += r1.z; v[7] += r1.w;
     *(float4*)(e.out + idx) = make_float4(v[0], v[1], v[2], v[3]);
     *(float4*)(e.out + idx + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// Gains of 8 columns n..n+7, loaded ahead of the residual stores (see
+// epi_norm_operand_g), for epi_norm_operand8g.
+LLB_DEV void epi_gain8(const Epilogue& e, int n, float* g) {
+    *(float4*)&g[0] = *(const float4*)(e.gain + n);
+    *(float4*)&g[4] = *(const float4*)(e.gain + n + 4);
+}
+
+// bf16(h * g) for 8 columns with the gains loaded ahead; returns the sum of h^2.
+LLB_DEV float epi_norm_operand8g(const Epilogue& e, int m, int n, int N, const float* h, const float* g) {
+    float t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t[k] = h[k] * g[k];
+    *(uint4*)((bf16_t*)e.a_out + (size_t)m * N + n) = pack8(t);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += h[k] * h[k];
+    return s;
 }
 
 // bf16(h * g) for 8 columns; returns the sum of h^2 over them.

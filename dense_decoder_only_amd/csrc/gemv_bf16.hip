@@ -108,15 +108,17 @@ LLB_DEV void gemv_tile_epilogue(const GemmArgs& args, const float* sred, const f
     const int wave = tid >> 6;
     const Epilogue& e = args.epi;
     if constexpr (EPI == EPI_RESID_NORM) {
-        // two rows per pass, 128 threads (two waves) per row
+        // two rows per pass, 128 threads (two waves) per row; a thread's column
+        // (and gain) is the same in every pass
         __shared__ float s_ss[4];
+        const float g = e.gain[n0 + (tid & 127)];
         for (int m0r = 0; m0r < M; m0r += 2) {
             const int m = m0r + (tid >> 7);
             const int c = tid & 127;
             float ss = 0.f;
             if (m < M) {
                 const float h = epi_resid(e, m, n0 + c, N, sred[m * GV_BN + c]);
-                epi_norm_operand(e, m, n0 + c, N, h);
+                epi_norm_operand_g(e, m, n0 + c, N, h, g);
                 ss = h * h;
             }
             ss = warp_sum(ss);
@@ -321,9 +323,10 @@ gemv_reduce_kernel(GemmArgs args, int splits, const float* __restrict__ part) {
     if constexpr (EPI == EPI_RESID_NORM) {
         __shared__ float s_ss[4];
         float ss = 0.f;
+        const float g = e.gain[n0 + j];
         if (m < M) {
             const float h = epi_resid(e, m, n0 + j, N, col(j));
-            epi_norm_operand(e, m, n0 + j, N, h);
+            epi_norm_operand_g(e, m, n0 + j, N, h, g);
             ss = h * h;
         }
         ss = warp_sum(ss);
@@ -607,10 +610,12 @@ gemv_narrow_kernel(GemmArgs args) {
         }
     } else {  // EPI_RESID_NORM: h, the next RMSNorm's operand, sum of h^2 over the RW columns
         float ss = 0.f;
+        float g[8];
+        epi_gain8(e, n0 + c0, g);
         if (m < M) {
             cols8(m, c0, v);
             epi_resid8(e, m, n0 + c0, N, v);
-            ss = epi_norm_operand8(e, m, n0 + c0, N, v);
+            ss = epi_norm_operand8g(e, m, n0 + c0, N, v, g);
         }
 #pragma unroll
         for (int o = TPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
