@@ -1,10 +1,13 @@
-// Large-M bf16 projection C = A . W^T on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
+// Large-M bf16 projection C = A . W^T on gfx950 MFMA (v_mfma_f32_32x32x16_bf16
+// or v_mfma_f32_16x16x32_bf16, per schedule).
 //
-// Both operands are bf16 and K-contiguous ([rows][K] row-major).  Tiles of
-// BM x BK (A) and BN x BK (W) are copied global -> LDS by the DMA path of the
-// vector memory unit (global_load_lds_dwordx4: each lane's 16 bytes land in LDS
-// without passing through registers), STAGES k-tiles ahead of the MFMAs.  The
-// only synchronisation per k-tile is one `s_waitcnt vmcnt(n)` that retires the
+// Both operands are bf16 and K-contiguous: A row-major [M][K], W in 128-row x
+// 64-column tiles (see tile_weights_launch), so that one k-tile of a 128-row
+// block of W is 16 KB of contiguous memory.  Tiles of BM x BK (A) and BN x BK
+// (W) are copied global -> LDS by the DMA path of the vector memory unit
+// (global_load_lds_dwordx4: each lane's 16 bytes land in LDS without passing
+// through registers), STAGES - 1 k-tiles ahead of the MFMAs.  The only
+// synchronisation per k-tile is one `s_waitcnt vmcnt(n)` that retires the
 // oldest stage's copies and one workgroup barrier.
 //
 // LDS rows are BK bf16 (BK = 32: 64 bytes, four 16-byte chunks).  Chunk c of
