@@ -388,7 +388,10 @@ gemm_bf16_kernel(GemmArgs args) {
         for (int n = 0; n < NR; ++n) rd(a_off[0], b_off[0], 0, n);
         // copies per step of 0..KS-2 (the last step carries none)
         constexpr int CPS = (L - CA + KS - 2) / (KS - 1);
-        constexpr int HALF = NM / 2;
+        // MFMAs of the last k-step before the copy wait: half, or five eighths on
+        // the W-only-prefetch kernels, whose copies of W land later (the gate/up
+        // projections: 0.8% faster; half is best with both prefetches)
+        constexpr int HALF = (SCHED & SCHED_PF_W_ONLY) ? NM * 5 / 8 : NM / 2;
         // The body is the same for every k-tile: near the end, the copies of
         // "k-tile t+STAGES-1" repeat the last k-tile into the free stage and
         // the reads of "k-tile t+1" land in registers that are not used again.
