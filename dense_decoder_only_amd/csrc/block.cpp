@@ -310,7 +310,9 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 //    kernel with the prefetch at large N and the 8-wave kernel otherwise; the
 //    gate/up projection, whose band of A panels stays in the last-level cache
 //    over 14 column blocks, prefetches W lines only (70B gate/up -2%; the
-//    down projection, whose A streams from HBM, is 5% slower that way);
+//    down projection, whose A streams from HBM, is 5% slower that way), and
+//    so does the output projection with the next norm's operand (70B O
+//    -1.6%);
 //  - 256x192 tiles when they fill whole rounds of the 256 compute units (the
 //    QKV projection on the 16x16x32 spread-copy kernel prefetching W lines
 //    only, the whole A being cache-resident at these sizes (8B QKV -4%);
@@ -329,8 +331,8 @@ int pick_tile(int M, int N, int K, int epi) {
     if (!llb::gemm_bf16_offsets_fit(M, N, K))  // beyond the interleaved schedules' reach
         return N % 256 == 0 ? 0 : N % 128 != 0 ? -1 : M > 128 ? 1 : 2;
     if (N % 256 == 0 && M >= 4096)
-        return epi == llb::EPI_SWIGLU ? 17
-               : (scaled || K >= 16384 || epi == llb::EPI_RESID_NORM) ? 14 : N >= 32768 ? 4 : 0;
+        return (epi == llb::EPI_SWIGLU || epi == llb::EPI_RESID_NORM) ? 17
+               : (scaled || K >= 16384) ? 14 : N >= 32768 ? 4 : 0;
     if (N % 128 != 0) return -1;
     if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 18 : 6;
     if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 17 : 0;
