@@ -28,7 +28,7 @@ Sources (page title, section):
        apply_rotary_emb, forward(tokens, start_pos)), layers.py excerpts
        (weights stored [out, in], F.linear computes x A^T).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * llama3 frequency scaling: the pages only say that the fastest rotations
     are kept, the slowest are slowed by the factor (8) and an intermediate
     band is blended.  Reading: wavelength lambda = 2*pi/omega; keep omega if

@@ -15,7 +15,7 @@ Prepare Q, K, V": forward(tokens, start_pos) with one cache per layer):
                                           layer l's cache at start_pos)
   logits = RMSNorm(x_L; g_final) W_out^T (W_out [vocab, d], not tied to E)
 
-Reading (also in the design doc): the pages show the LM head on every position; a
+Reading: the pages show the LM head on every position; a
 caller that samples only needs each sequence's last position, which is the
 same rows of the same product (`last_only`).
 """
