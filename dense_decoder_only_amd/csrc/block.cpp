@@ -321,8 +321,9 @@ WsPlan plan_ws(const llb_block* b, int B, int T, bool decode, int n_keys) {
 //    16x16x32 spread-copy kernel prefetching W lines only, 8B gate/up -3%;
 //    the rest on the 8-wave kernel);
 //  - 256x128 tiles (interleaved, BK 64, 3 stages; spread copies for the
-//    residual-only epilogue, the down projection) from 192 tiles up when K is
-//    a multiple of 64; two 256x128 or 128x128 workgroups per CU below that;
+//    residual epilogues, the down and output projections: 8B O -3%) from 192
+//    tiles up when K is a multiple of 64; two 256x128 or 128x128 workgroups
+//    per CU below that;
 //  - operands past 4 GiB (beyond the interleaved kernels' 32-bit offsets): the
 //    plain 8-wave or 256x128 / 128x128 kernels.
 int pick_tile(int M, int N, int K, int epi) {
@@ -337,7 +338,7 @@ int pick_tile(int M, int N, int K, int epi) {
     if (N % 192 == 0 && K % 64 == 0 && ((long)pm * (N / 192)) % 256 == 0) return epi == llb::EPI_QKV ? 18 : 6;
     if (N % 256 == 0 && (long)pm * (N / 256) >= 160) return epi == llb::EPI_SWIGLU ? 17 : 0;
     const long t128 = (long)pm * (N / 128);
-    if (t128 >= 192 && K % 64 == 0) return epi == llb::EPI_RESID ? 16 : 7;
+    if (t128 >= 192 && K % 64 == 0) return (epi == llb::EPI_RESID || epi == llb::EPI_RESID_NORM) ? 16 : 7;
     return M > 128 ? 1 : 2;
 }
 
