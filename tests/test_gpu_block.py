@@ -180,6 +180,26 @@ def test_bf16_prefill_column_interleaved_tile_order(T):
     assert torch.all(kd[:, :, T:].float() == SENTINEL)
 
 
+# Long inputs (M >= 4096 rows) take the 256 x 256 kernels that prefetch W lines
+# only for the gate/up and output projections, and A and W lines for QKV and
+# the long-K down projection (K = d_ff = 16384); T = 4100 leaves a 4-row last
+# row panel on all four, and 17 row panels
+# that no block tile order divides.  y is compared on sampled rows (the causal
+# block makes each row's output depend only on the rows before it), including
+# the last panel's; K and V on every row.
+def test_bf16_prefill_long_ragged_rows():
+    shp = shape(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=16384, rope_scaling=True)
+    T = 4100
+    rows = [0, 1, 255, 256, 2047, 2048, 4095, 4096, 4097, 4099]
+    y, kd, vd, y_ref, k_ref, v_ref = _run_prefill(shp, 4100, 1, T, rows=rows)
+    e_y = rel_err(y, y_ref)
+    e_k = bf16_err(kd[:, :, :T], k_ref)
+    e_v = bf16_err(vd[:, :, :T], v_ref)
+    note(f"  y {e_y:.2e}  k {e_k:.3f}  v {e_v:.3f}")
+    assert e_y <= 2e-2 and e_k <= 1.0 and e_v <= 1.0
+    assert torch.all(kd[:, :, T:].float() == SENTINEL)
+
+
 def test_tile_override_rejects_bad_values():
     from dense_decoder_only_amd import llb
     shp = shape(**TILE_SHAPE, rope_scaling=False)
